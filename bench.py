@@ -1,0 +1,252 @@
+"""Benchmark of the MoE dispatch / combine hot path on one MI355X.
+
+One step = layout (count, scan, place) + fp8 packed dispatch + bf16 combine
+over the 8192-token, hidden-7168, top-8-of-256-experts workload, with every
+input already resident in HBM.  Prints one JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+Per-op times come from HIP events recorded on the stream the kernels run on
+(torch's current stream, which the binding passes to every entry point).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+METRIC = "dispatch / combine µs and achieved HBM GB/s (% of peak), 8192×7168 top-8 E=256"
+
+
+def algorithmic_bytes(T, H, K, E, n_sel, fp8_row_bytes):
+    """Bytes each op must move at minimum (reads + writes), per launch."""
+    layout = T * K * 8 + T * K * 4 + (2 * E + 1) * 4  # idx in, slot out, counts/offsets
+    disp_fp8 = T * H * 2 + T * K * 4 + n_sel * fp8_row_bytes  # x in, slot in, rows out
+    disp_bf16 = T * H * 2 + T * K * 4 + n_sel * H * 2
+    combine = n_sel * H * 2 + T * K * (4 + 4) + T * H * 2  # y rows in, slot+w in, out
+    return {"layout": layout, "dispatch_fp8": disp_fp8, "dispatch_bf16": disp_bf16, "combine": combine}
+
+
+def cpu_baseline(w, idx, wt, x_host, y_host, sample_tokens):
+    """The CPU oracle, as it stands, timed on a bounded sample of the workload:
+    the full layout, then fp8 dispatch and combine of the first
+    ``sample_tokens`` tokens.  Reported in the metric's unit (GB/s of the
+    same algorithmic bytes)."""
+    import numpy as np
+
+    from oracle import ep_oracle as O
+
+    threads = 1  # numpy's elementwise, indexing and searchsorted kernels run on one thread
+    t0 = time.perf_counter()
+    R = O.layout(idx, w.E)
+    t1 = time.perf_counter()
+    S = sample_tokens
+    slot_s = R["slot"][:S]
+    used = np.unique(slot_s[slot_s >= 0])
+    remap = -np.ones(R["n_sel"] + 1, np.int64)
+    remap[used] = np.arange(len(used))
+    slot_r = np.where(slot_s >= 0, remap[np.maximum(slot_s, 0)], -1)
+    rb = O.fp8_row_bytes(w.H)
+    t2 = time.perf_counter()
+    O.dispatch_fp8(x_host[:S], slot_r, len(used))
+    t3 = time.perf_counter()
+    ysub = y_host[used]
+    t4 = time.perf_counter()
+    O.combine(ysub, slot_r, wt[:S])
+    t5 = time.perf_counter()
+    b_layout = w.T * w.K * 12
+    b_disp = S * w.H * 2 + S * w.K * 4 + len(used) * rb
+    b_comb = len(used) * w.H * 2 + S * w.K * 8 + S * w.H * 2
+    secs = (t1 - t0) + (t3 - t2) + (t5 - t4)
+    return {
+        "value": round((b_layout + b_disp + b_comb) / secs / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"full layout of {w.T}x{w.K} ids; fp8 dispatch + combine of the first {S} tokens "
+        f"({len(used)} rows); {secs:.1f} s of CPU time; numpy single-threaded elementwise",
+        "seconds": {"layout": round(t1 - t0, 3), "dispatch_fp8": round(t3 - t2, 3), "combine": round(t5 - t4, 3)},
+        "cpu_model": platform.processor() or platform.machine(),
+        "host_cpu_count": os.cpu_count(),
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="pages")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
+    ap.add_argument("--bf16-dispatch", action="store_true", help="also time the bf16 dispatch variant")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(
+            f"bench.py measures one GPU's share of dispatch/combine; --gpus {args.gpus} is not "
+            "supported (no collectives in this build)",
+            file=sys.stderr,
+        )
+        return 2
+
+    import numpy as np
+    import torch
+
+    import combine_ep_layout_03_amd as ep
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    w = W.by_name(args.workload)
+    T, H, K, E = w.T, w.H, w.K, w.E
+    print(f"# workload {w.name}: T={T} H={H} K={K} E={E}; generating inputs", file=sys.stderr, flush=True)
+    idx, wt = W.make_routing(w)
+    d_idx, d_wt = idx.to(dev), wt.to(dev)
+    x = W.make_x(w, device=dev)
+    y = W.make_y(w, device=dev)  # T*K expert-output rows
+    rb = ep.ep_fp8_row_bytes(H)
+
+    L = ep.ep_layout(d_idx, E)
+    n_sel = L.num_rows()
+    recv8 = torch.empty(T * K, rb, dtype=torch.uint8, device=dev)
+    out = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    recv16 = torch.empty(T * K, H, dtype=torch.bfloat16, device=dev) if args.bf16_dispatch else None
+    nb = algorithmic_bytes(T, H, K, E, n_sel, rb)
+
+    stream = torch.cuda.current_stream(dev)
+    ev = {k: [] for k in ("start", "layout", "dispatch", "combine", "bf16")}
+
+    def step(record):
+        if record:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+        ep.ep_layout(d_idx, E, out=L)
+        if record:
+            e1 = torch.cuda.Event(enable_timing=True)
+            e1.record(stream)
+        ep.ep_dispatch(x, L, fp8=True, out=recv8)
+        if record:
+            e2 = torch.cuda.Event(enable_timing=True)
+            e2.record(stream)
+        ep.ep_combine(y, L, d_wt, out=out)
+        if record:
+            e3 = torch.cuda.Event(enable_timing=True)
+            e3.record(stream)
+            ev["start"].append(e0)
+            ev["layout"].append(e1)
+            ev["dispatch"].append(e2)
+            ev["combine"].append(e3)
+        if recv16 is not None:
+            ep.ep_dispatch(x, L, fp8=False, out=recv16)
+            if record:
+                e4 = torch.cuda.Event(enable_timing=True)
+                e4.record(stream)
+                ev["bf16"].append(e4)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    print(f"# warmup done; timing {args.steps} steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    def ms(a, b):
+        return [x.elapsed_time(y) for x, y in zip(ev[a], ev[b])]
+
+    t_layout = ms("start", "layout")
+    t_disp = ms("layout", "dispatch")
+    t_comb = ms("dispatch", "combine")
+    t_step = [a + b + c for a, b, c in zip(t_layout, t_disp, t_comb)]
+    t_bf16 = ms("combine", "bf16") if recv16 is not None else []
+
+    def stats(v, nbytes):
+        med = statistics.median(v)
+        return {
+            "us_median": round(med * 1e3, 2),
+            "us_min": round(min(v) * 1e3, 2),
+            "us_max": round(max(v) * 1e3, 2),
+            "bytes": nbytes,
+            "GBps": round(nbytes / (med * 1e-3) / 1e9, 1),
+            "pct_of_peak": round(100.0 * nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
+        }
+
+    ops = {
+        "layout": stats(t_layout, nb["layout"]),
+        "dispatch_fp8": stats(t_disp, nb["dispatch_fp8"]),
+        "combine": stats(t_comb, nb["combine"]),
+    }
+    if t_bf16:
+        ops["dispatch_bf16"] = stats(t_bf16, nb["dispatch_bf16"])
+    step_bytes = nb["layout"] + nb["dispatch_fp8"] + nb["combine"]
+    step_ms = statistics.median(t_step)
+    value = step_bytes / (step_ms * 1e-3) / 1e9
+
+    # roofline of the dominant kernel (largest median time of the step's ops)
+    dom = max(("dispatch_fp8", "combine"), key=lambda k: ops[k]["us_median"])
+    avg_us = statistics.mean(t_disp if dom == "dispatch_fp8" else t_comb) * 1e3
+    achieved = nb[dom] / (avg_us * 1e-6) / 1e9
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", f"traffic_{dom}_{w.name}.json")
+    if os.path.exists(tfile):
+        with open(tfile) as fh:
+            traffic = json.load(fh).get("bytes_per_launch")
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3+bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: T={T} tokens, H={H}, top-{K} of E={E} experts, uniform routing; "
+            "fp8 packed dispatch + bf16 combine",
+            "global_batch": T,
+            "seq_len": 1,
+            "parallelism": "single-GPU",
+        },
+        "ops": ops,
+        "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": dom,
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "avg_launch_us": round(avg_us, 2),
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("# timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        x_host = x.cpu().view(torch.int16).numpy().view(np.uint16)
+        S = args.cpu_sample_tokens
+        y_host = y[: int(n_sel)].cpu().view(torch.int16).numpy().view(np.uint16)
+        res["cpu_baseline"] = cpu_baseline(w, idx.numpy(), wt.numpy(), x_host, y_host, S)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,288 @@
+"""MoE token dispatch / combine for one MI355X (gfx950).
+
+A thin binding over the C ABI in include/ep_mi355x.h: each function checks
+that the torch tensors it is handed are contiguous device tensors of the
+right dtype and shape, allocates outputs with torch (device memory is the
+only thing torch provides here), and calls the library entry point of the
+same name on torch's current stream.  Every step of the path runs in the HIP
+kernels; there is no CPU or PyTorch fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+
+import torch
+
+from . import _lib
+from ._lib import (  # noqa: F401
+    EP_COMBINE_FLAT,
+    EP_COMBINE_GROUPED,
+    EP_FORMAT_BF16,
+    EP_FORMAT_FP8_PACKED,
+    EP_ROWS_EXPERT,
+    EP_ROWS_GROUP,
+    EP_STATUS_COMBINE_OOB,
+    EP_STATUS_INVALID_IDS,
+    EP_STATUS_LIST_OVERFLOW,
+    EP_STATUS_ROWS_EXPERT,
+    EP_STATUS_ROWS_GROUP,
+    EP_STATUS_WORDS,
+    EPError,
+)
+
+__all__ = [
+    "Layout",
+    "ep_fp8_row_bytes",
+    "ep_layout_workspace_bytes",
+    "ep_layout",
+    "ep_dispatch",
+    "ep_combine",
+    "ep_strerror",
+    "EPError",
+]
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t: torch.Tensor, name: str, dtype: torch.dtype, shape=None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _problem(T: int, H: int, K: int, E: int, G: int) -> _lib.Problem:
+    return _lib.Problem(T, H, K, E, G)
+
+
+def ep_fp8_row_bytes(hidden: int) -> int:
+    """Bytes of one packed fp8 row (H payload bytes, H/128 fp32 scales, 16-byte pad)."""
+    return int(_lib.lib().ep_fp8_row_bytes(hidden))
+
+
+def ep_layout_workspace_bytes(num_tokens: int, topk: int, num_experts: int, num_groups: int = 0) -> int:
+    p = _problem(num_tokens, 1, topk, num_experts, num_groups)
+    return int(_lib.lib().ep_layout_workspace_bytes(ctypes.byref(p)))
+
+
+def ep_strerror(code: int) -> str:
+    return _lib.lib().ep_strerror(code).decode()
+
+
+@dataclasses.dataclass
+class Layout:
+    """Device outputs of ep_layout plus the shape they were computed for."""
+
+    num_tokens: int
+    topk: int
+    num_experts: int
+    num_groups: int
+    counts: torch.Tensor
+    offsets: torch.Tensor
+    slot: torch.Tensor
+    status: torch.Tensor
+    group_counts: torch.Tensor | None = None
+    group_offsets: torch.Tensor | None = None
+    grow: torch.Tensor | None = None
+    row_src: torch.Tensor | None = None
+    row_topk_idx: torch.Tensor | None = None
+    row_topk_weights: torch.Tensor | None = None
+    row_capacity: int = 0
+    workspace: torch.Tensor | None = None
+
+    def struct(self) -> _lib.LayoutStruct:
+        return _lib.LayoutStruct(
+            _ptr(self.counts),
+            _ptr(self.offsets),
+            _ptr(self.slot),
+            _ptr(self.status),
+            _ptr(self.group_counts),
+            _ptr(self.group_offsets),
+            _ptr(self.grow),
+            _ptr(self.row_src),
+            _ptr(self.row_topk_idx),
+            _ptr(self.row_topk_weights),
+            self.row_capacity,
+        )
+
+    def max_group_rows(self) -> int:
+        return min(self.num_tokens * self.num_groups, self.num_tokens * self.topk)
+
+    def num_rows(self, rows: int = EP_ROWS_EXPERT) -> int:
+        """Rows the layout needs (synchronises the stream)."""
+        w = EP_STATUS_ROWS_EXPERT if rows == EP_ROWS_EXPERT else EP_STATUS_ROWS_GROUP
+        return int(self.status[w].item())
+
+
+def ep_layout(
+    topk_idx: torch.Tensor,
+    num_experts: int,
+    num_groups: int = 0,
+    topk_weights: torch.Tensor | None = None,
+    row_capacity: int | None = None,
+    out: Layout | None = None,
+) -> Layout:
+    """Count, scan and place every selection of topk_idx (int64 [T, K]).
+
+    ``out`` reuses the buffers of an earlier Layout of the same shape
+    (nothing is allocated then)."""
+    if topk_idx.dim() != 2:
+        raise ValueError("topk_idx must be [T, K]")
+    T, K = topk_idx.shape
+    _dev(topk_idx, "topk_idx", torch.int64)
+    dev = topk_idx.device
+    G = int(num_groups)
+    if topk_weights is not None:
+        _dev(topk_weights, "topk_weights", torch.float32, (T, K))
+    if out is not None:
+        if (out.num_tokens, out.topk, out.num_experts, out.num_groups) != (T, K, num_experts, G):
+            raise ValueError("out was allocated for a different problem shape")
+        if G > 0 and topk_weights is None:
+            raise ValueError("grouped layout needs topk_weights for the per-row weight lists")
+        _run_layout(out, topk_idx, topk_weights)
+        return out
+    i32 = dict(dtype=torch.int32, device=dev)
+    L = Layout(
+        num_tokens=T,
+        topk=K,
+        num_experts=num_experts,
+        num_groups=G,
+        counts=torch.empty(num_experts, **i32),
+        offsets=torch.empty(num_experts + 1, **i32),
+        slot=torch.empty(T, K, **i32),
+        status=torch.empty(_lib.EP_STATUS_WORDS, **i32),
+    )
+    if G > 0:
+        cap = L.max_group_rows() if row_capacity is None else int(row_capacity)
+        L.row_capacity = cap
+        L.group_counts = torch.empty(G, **i32)
+        L.group_offsets = torch.empty(G + 1, **i32)
+        L.grow = torch.empty(T, K, **i32)
+        L.row_src = torch.empty(max(cap, 1), **i32)
+        L.row_topk_idx = torch.empty(max(cap, 1), K, **i32)
+        L.row_topk_weights = torch.empty(max(cap, 1), K, dtype=torch.float32, device=dev)
+        if topk_weights is None:
+            raise ValueError("grouped layout needs topk_weights for the per-row weight lists")
+    p = _problem(T, 1, K, num_experts, G)
+    nbytes = int(_lib.lib().ep_layout_workspace_bytes(ctypes.byref(p)))
+    if nbytes == 0:
+        raise _lib.EPError("ep_layout_workspace_bytes", _lib.EP_EINVAL, "invalid problem shape")
+    L.workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    _run_layout(L, topk_idx, topk_weights)
+    return L
+
+
+def _run_layout(L: Layout, topk_idx: torch.Tensor, topk_weights: torch.Tensor | None) -> None:
+    p = _problem(L.num_tokens, 1, L.topk, L.num_experts, L.num_groups)
+    s = L.struct()
+    rc = _lib.lib().ep_layout(
+        ctypes.byref(p),
+        _ptr(topk_idx),
+        _ptr(topk_weights),
+        ctypes.byref(s),
+        _ptr(L.workspace),
+        L.workspace.numel(),
+        _stream(topk_idx.device),
+    )
+    _lib.check("ep_layout", rc)
+
+
+def ep_dispatch(
+    x: torch.Tensor,
+    layout: Layout,
+    fp8: bool = False,
+    rows: int = EP_ROWS_EXPERT,
+    capacity: int | None = None,
+    out: torch.Tensor | None = None,
+) -> torch.Tensor:
+    """Scatter token rows x (bf16 [T, H]) to their receive rows.
+
+    Returns ``out``: bf16 [capacity, H], or uint8 [capacity, ep_fp8_row_bytes(H)]
+    with ``fp8``.  The default capacity is the worst case (T*K expert rows,
+    min(T*G, T*K) group rows), so no host synchronisation is needed."""
+    if x.dim() != 2 or x.shape[0] != layout.num_tokens:
+        raise ValueError("x must be [T, H] with the layout's T")
+    _dev(x, "x", torch.bfloat16)
+    T, H = x.shape
+    if capacity is None:
+        capacity = T * layout.topk if rows == EP_ROWS_EXPERT else layout.max_group_rows()
+    fmt = EP_FORMAT_FP8_PACKED if fp8 else EP_FORMAT_BF16
+    if out is None:
+        if fp8:
+            rb = ep_fp8_row_bytes(H)
+            if rb < 0:
+                raise _lib.EPError("ep_dispatch", _lib.EP_ENOTSUP, "fp8 rows need hidden % 128 == 0")
+            out = torch.empty(max(capacity, 1), rb, dtype=torch.uint8, device=x.device)
+        else:
+            out = torch.empty(max(capacity, 1), H, dtype=torch.bfloat16, device=x.device)
+    else:
+        if fp8:
+            _dev(out, "out", torch.uint8)
+            if out.dim() != 2 or out.shape[1] != ep_fp8_row_bytes(H) or out.shape[0] < capacity:
+                raise ValueError("out must be uint8 [>= capacity, ep_fp8_row_bytes(H)]")
+        else:
+            _dev(out, "out", torch.bfloat16)
+            if out.dim() != 2 or out.shape[1] != H or out.shape[0] < capacity:
+                raise ValueError("out must be bf16 [>= capacity, H]")
+    p = _problem(T, H, layout.topk, layout.num_experts, layout.num_groups)
+    s = layout.struct()
+    rc = _lib.lib().ep_dispatch(
+        ctypes.byref(p), ctypes.byref(s), _ptr(x), _ptr(out), int(capacity), int(rows), fmt, _stream(x.device)
+    )
+    _lib.check("ep_dispatch", rc)
+    return out
+
+
+def ep_combine(
+    y: torch.Tensor,
+    layout: Layout,
+    topk_weights: torch.Tensor,
+    topk_idx: torch.Tensor | None = None,
+    order: int = EP_COMBINE_FLAT,
+    out: torch.Tensor | None = None,
+) -> torch.Tensor:
+    """Weighted reduction of each token's expert-output rows y (bf16 [rows, H],
+    expert-major) into out (bf16 [T, H])."""
+    if y.dim() != 2:
+        raise ValueError("y must be [rows, H]")
+    _dev(y, "y", torch.bfloat16)
+    T, K = layout.num_tokens, layout.topk
+    H = y.shape[1]
+    _dev(topk_weights, "topk_weights", torch.float32, (T, K))
+    if topk_idx is not None:
+        _dev(topk_idx, "topk_idx", torch.int64, (T, K))
+    if order == EP_COMBINE_GROUPED and topk_idx is None:
+        raise ValueError("grouped order needs topk_idx")
+    if out is None:
+        out = torch.empty(T, H, dtype=torch.bfloat16, device=y.device)
+    else:
+        _dev(out, "out", torch.bfloat16, (T, H))
+    p = _problem(T, H, K, layout.num_experts, layout.num_groups)
+    s = layout.struct()
+    rc = _lib.lib().ep_combine(
+        ctypes.byref(p),
+        ctypes.byref(s),
+        _ptr(topk_idx),
+        _ptr(topk_weights),
+        _ptr(y),
+        int(y.shape[0]),
+        _ptr(out),
+        int(order),
+        _stream(y.device),
+    )
+    _lib.check("ep_combine", rc)
+    return out

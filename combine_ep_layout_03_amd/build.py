@@ -1,0 +1,62 @@
+"""Build the HIP library in-tree: combine_ep_layout_03_amd/libep_mi355x.so.
+
+One hipcc invocation for gfx950 only.  Floating-point flags matter for
+bit-exact results: no contraction of a*b+c into FMA, correctly rounded fp32
+division, fp32 denormals kept, no fast-math, and no packed-fp32 instructions.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_NAME = "libep_mi355x.so"
+LIB_PATH = os.path.join(HERE, LIB_NAME)
+
+SOURCES = ["ep_api.hip", "ep_layout.hip", "ep_dispatch.hip", "ep_combine.hip"]
+
+HIPCC_FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    "-ffp-contract=off",
+    "-fno-fast-math",
+    "-fhip-fp32-correctly-rounded-divide-sqrt",
+    "-fno-gpu-flush-denormals-to-zero",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall",
+]
+
+
+def hipcc() -> str:
+    path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(path):
+        raise RuntimeError("hipcc not found; the HIP library cannot be built")
+    return path
+
+
+def build(verbose: bool = False, extra_flags: list[str] | None = None, out: str | None = None) -> str:
+    """Compile every source into the shared library and return its path."""
+    out = out or LIB_PATH
+    tmp = out + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), "-I", INCLUDE, "-I", CSRC]
+    cmd += [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}\n{res.stderr}")
+    if verbose and (res.stdout or res.stderr):
+        print(res.stdout, res.stderr, flush=True)
+    os.replace(tmp, out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

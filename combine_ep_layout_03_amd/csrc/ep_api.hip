@@ -1,0 +1,179 @@
+// C-ABI entry points: argument checks, launch shapes, error codes.
+// Semantics of every call are documented in include/ep_mi355x.h.
+#include <limits.h>
+#include <stdint.h>
+
+#include "ep_internal.h"
+#include "ep_mi355x.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Basic shape checks shared by every call.
+int check_problem(const ep_problem_t* p) {
+  if (!p) return EP_EINVAL;
+  if (p->num_tokens < 0 || p->hidden < 1 || p->topk < 1 || p->num_experts < 1 ||
+      p->num_groups < 0)
+    return EP_EINVAL;
+  if (p->num_groups > 0 && p->num_experts % p->num_groups != 0) return EP_EINVAL;
+  if (p->topk > EP_MAX_TOPK) return EP_ENOTSUP;
+  if (static_cast<int64_t>(p->num_experts) + p->num_groups > EP_MAX_KEYS) return EP_ENOTSUP;
+  // slots and rows are int32: every (t,k) must index below 2^31
+  if (p->num_tokens > static_cast<int64_t>(INT32_MAX) / p->topk) return EP_ENOTSUP;
+  return EP_OK;
+}
+
+// Widest vector (bytes) that divides `row_bytes` and the alignment of both bases.
+int vec_bytes_for(int64_t row_bytes, const void* a, const void* b) {
+  for (int v = 16; v > 2; v >>= 1)
+    if (row_bytes % v == 0 && aligned(a, v) && aligned(b, v)) return v;
+  return 2;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t ep_fp8_row_bytes(int32_t hidden) {
+  if (hidden <= 0 || hidden % 128 != 0) return -1;
+  const int64_t raw = static_cast<int64_t>(hidden) + 4 * (hidden / 128);
+  return (raw + 15) / 16 * 16;
+}
+
+size_t ep_layout_workspace_bytes(const ep_problem_t* p) {
+  if (check_problem(p) != EP_OK) return 0;
+  const ep::LayoutGeom g =
+      ep::layout_geom(p->num_tokens * p->topk, p->num_experts, p->num_groups);
+  return ep::layout_workspace_bytes(g);
+}
+
+int ep_layout(const ep_problem_t* p, const int64_t* topk_idx, const float* topk_weights,
+              const ep_layout_t* L, void* workspace, size_t workspace_bytes,
+              hipStream_t stream) {
+  int rc = check_problem(p);
+  if (rc != EP_OK) return rc;
+  if (!L || !L->counts || !L->offsets || !L->status || !workspace) return EP_EINVAL;
+  const int64_t T = p->num_tokens;
+  const bool grouped = p->num_groups > 0;
+  if (T > 0 && (!topk_idx || !L->slot)) return EP_EINVAL;
+  if (grouped) {
+    if (!L->group_counts || !L->group_offsets || (T > 0 && !L->grow)) return EP_EINVAL;
+    if (L->row_capacity < 0) return EP_EINVAL;
+    if (L->row_capacity > 0 && T > 0 &&
+        (!L->row_src || !L->row_topk_idx || !L->row_topk_weights || !topk_weights))
+      return EP_EINVAL;
+  }
+  if (!aligned(topk_idx, 8) || !aligned(workspace, 4)) return EP_EINVAL;
+
+  const ep::LayoutGeom g = ep::layout_geom(T * p->topk, p->num_experts, p->num_groups);
+  if (workspace_bytes < ep::layout_workspace_bytes(g)) return EP_EWORKSPACE;
+
+  ep::LayoutArgs a;
+  a.idx = topk_idx;
+  a.w = topk_weights;
+  a.n = static_cast<uint32_t>(T * p->topk);
+  a.K = p->topk;
+  a.E = p->num_experts;
+  a.G = p->num_groups;
+  a.epg = grouped ? p->num_experts / p->num_groups : 1;
+  a.counts = L->counts;
+  a.offsets = L->offsets;
+  a.slot = L->slot;
+  a.status = L->status;
+  a.gcounts = L->group_counts;
+  a.goffsets = L->group_offsets;
+  a.grow = L->grow;
+  a.row_src = L->row_src;
+  a.row_idx = L->row_topk_idx;
+  a.row_w = L->row_topk_weights;
+  a.row_cap = grouped ? L->row_capacity : 0;
+  a.partials = static_cast<int32_t*>(workspace);
+  return ep::launch_layout(a, g, stream) == hipSuccess ? EP_OK : EP_EHIP;
+}
+
+int ep_dispatch(const ep_problem_t* p, const ep_layout_t* L, const void* x, void* recv,
+                int64_t capacity_rows, int32_t rows, int32_t format, hipStream_t stream) {
+  int rc = check_problem(p);
+  if (rc != EP_OK) return rc;
+  if (!L || !L->status || capacity_rows < 0) return EP_EINVAL;
+  if (rows != EP_ROWS_EXPERT && rows != EP_ROWS_GROUP) return EP_EINVAL;
+  if (format != EP_FORMAT_BF16 && format != EP_FORMAT_FP8_PACKED) return EP_EINVAL;
+  if (rows == EP_ROWS_GROUP && p->num_groups < 1) return EP_EINVAL;
+  int64_t fp8_rb = 0;
+  if (format == EP_FORMAT_FP8_PACKED) {
+    fp8_rb = ep_fp8_row_bytes(p->hidden);
+    if (fp8_rb < 0) return EP_ENOTSUP;
+  }
+  if (p->num_tokens == 0) return EP_OK;
+  const int32_t* dest = rows == EP_ROWS_EXPERT ? L->slot : L->grow;
+  if (!dest || !x || (!recv && capacity_rows > 0)) return EP_EINVAL;
+  if (!aligned(x, 2) || !aligned(recv, 2)) return EP_EINVAL;
+
+  ep::ScatterArgs a;
+  a.x = x;
+  a.recv = recv;
+  a.dest = dest;
+  a.rows_needed = L->status + (rows == EP_ROWS_EXPERT ? EP_STATUS_ROWS_EXPERT : EP_STATUS_ROWS_GROUP);
+  a.T = p->num_tokens;
+  a.K = p->topk;
+  a.H = p->hidden;
+  a.capacity = capacity_rows;
+  a.dedup = rows == EP_ROWS_GROUP;
+  hipError_t err;
+  if (format == EP_FORMAT_FP8_PACKED) {
+    if (!aligned(x, 16) || !aligned(recv, 16)) return EP_EINVAL;
+    err = ep::launch_scatter_fp8(a, fp8_rb, stream);
+  } else {
+    err = ep::launch_scatter_bf16(a, vec_bytes_for(static_cast<int64_t>(p->hidden) * 2, x, recv),
+                                  stream);
+  }
+  return err == hipSuccess ? EP_OK : EP_EHIP;
+}
+
+int ep_combine(const ep_problem_t* p, const ep_layout_t* L, const int64_t* topk_idx,
+               const float* topk_weights, const void* y, int64_t y_rows, void* out,
+               int32_t order, hipStream_t stream) {
+  int rc = check_problem(p);
+  if (rc != EP_OK) return rc;
+  if (!L || !L->status || y_rows < 0) return EP_EINVAL;
+  if (order != EP_COMBINE_FLAT && order != EP_COMBINE_GROUPED) return EP_EINVAL;
+  const bool grouped = order == EP_COMBINE_GROUPED;
+  if (grouped && p->num_groups < 1) return EP_EINVAL;
+  if (p->num_tokens == 0) return EP_OK;
+  if (!L->slot || !topk_weights || !out || (grouped && !topk_idx)) return EP_EINVAL;
+  if (!y && y_rows > 0) return EP_EINVAL;
+  if (!aligned(y, 2) || !aligned(out, 2) || !aligned(topk_weights, 4) ||
+      !aligned(topk_idx, 8))
+    return EP_EINVAL;
+
+  ep::CombineArgs a;
+  a.y = y;
+  a.y_rows = y_rows;
+  a.slot = L->slot;
+  a.w = topk_weights;
+  a.idx = topk_idx;
+  a.E = p->num_experts;
+  a.epg = grouped ? p->num_experts / p->num_groups : 1;
+  a.T = p->num_tokens;
+  a.K = p->topk;
+  a.H = p->hidden;
+  a.out = out;
+  a.status = L->status;
+  a.grouped = grouped;
+  const int ve = vec_bytes_for(static_cast<int64_t>(p->hidden) * 2, y ? y : out, out) / 2;
+  return ep::launch_combine(a, ve, stream) == hipSuccess ? EP_OK : EP_EHIP;
+}
+
+const char* ep_strerror(int code) {
+  switch (code) {
+    case EP_OK: return "ok";
+    case EP_EINVAL: return "invalid argument (null pointer, bad size or misaligned base)";
+    case EP_ENOTSUP: return "unsupported (fp8 needs hidden % 128 == 0; K <= 32; E + G <= 1024)";
+    case EP_EHIP: return "HIP launch failed";
+    case EP_EWORKSPACE: return "workspace smaller than ep_layout_workspace_bytes()";
+    default: return "unknown error code";
+  }
+}
+
+}  // extern "C"

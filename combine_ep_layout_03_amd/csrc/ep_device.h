@@ -1,0 +1,105 @@
+// Device helpers shared by the dispatch / combine kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ep {
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;  // threads per block for every kernel here
+constexpr int kWavesPerBlock = kBlock / kWave;
+
+// ---------------------------------------------------------------- bf16 / fp32
+__device__ __forceinline__ float bf16_lo(uint32_t two) {  // element 0 of a packed pair
+  return __uint_as_float(two << 16);
+}
+__device__ __forceinline__ float bf16_hi(uint32_t two) {  // element 1 of a packed pair
+  return __uint_as_float(two & 0xFFFF0000u);
+}
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// fp32 -> bf16, round to nearest, ties to even.  Adding 0x7FFF plus the
+// lowest kept bit to the pattern carries into the kept half exactly when the
+// dropped half exceeds one half ulp, or equals it with an odd kept half.
+// Finite inputs only (the sums here are finite); overflow yields infinity.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  const uint32_t b = __float_as_uint(f);
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// ---------------------------------------------------------------- E4M3FN
+// fp32 -> OCP E4M3FN code, round to nearest even, saturating at 448.
+//   |v| >= 448             -> 0x7E (largest finite; the format has no inf)
+//   |v| <  2^-6 (subnormal) -> round(|v| * 2^9) to an integer k in [0, 8];
+//                              k is the code (k = 8 is 2^-6, the first normal)
+//   otherwise               -> keep 3 mantissa bits, rounding on the 20
+//                              dropped bits, and rebias the exponent 127 -> 7
+// The sign bit is copied, so negative values rounding to zero give 0x80.
+// NaN is outside the domain.
+__device__ __forceinline__ uint32_t f32_to_e4m3fn_sat(float v) {
+  const uint32_t b = __float_as_uint(v);
+  const uint32_t sign = (b >> 24) & 0x80u;
+  const uint32_t m = b & 0x7FFFFFFFu;
+  // all three candidates, then a select (no divergent branches); the
+  // subnormal candidate is only chosen below 2^-6, where |v| * 2^9 < 8, and
+  // the clamp keeps the conversion defined everywhere else
+  const uint32_t sub =
+      static_cast<uint32_t>(__builtin_rintf(fminf(__uint_as_float(m) * 512.0f, 16.0f)));
+  const uint32_t nrm = ((m + 0x7FFFFu + ((m >> 20) & 1u)) >> 20) - (120u << 3);
+  uint32_t code = m < 0x3C800000u ? sub : nrm;  // 2^-6
+  code = m >= 0x43E00000u ? 0x7Eu : code;       // 448.0f
+  return code | sign;
+}
+
+// ---------------------------------------------------------------- wave utils
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int l = lane_id();
+  return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+__device__ __forceinline__ int readlane(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+
+template <typename T>
+__device__ __forceinline__ T nt_load(const T* p) {
+  return __builtin_nontemporal_load(p);
+}
+template <typename T>
+__device__ __forceinline__ void nt_store(T v, T* p) {
+  __builtin_nontemporal_store(v, p);
+}
+
+// Vectors used for row copies (clang extended vectors: one global
+// load/store instruction each).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <int N>
+struct VecOf;
+template <>
+struct VecOf<16> {
+  using type = u32x4;
+};
+template <>
+struct VecOf<8> {
+  using type = u32x2;
+};
+template <>
+struct VecOf<4> {
+  using type = uint32_t;
+};
+template <>
+struct VecOf<2> {
+  using type = uint16_t;
+};
+
+}  // namespace ep

@@ -1,0 +1,76 @@
+// Internal launch interface between the C-ABI entry points and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ep {
+
+// Geometry of the layout kernels: block b counts entries
+// [b * rounds * 256, (b + 1) * rounds * 256) of the flattened (t,k) order.
+struct LayoutGeom {
+  int nblocks;  // >= 1
+  int rounds;   // entries per thread
+  int ncols;    // E + G + 1 partial-count columns (last column: invalid ids)
+};
+
+LayoutGeom layout_geom(int64_t n_entries, int E, int G);
+size_t layout_workspace_bytes(const LayoutGeom& g);
+
+struct LayoutArgs {
+  const int64_t* idx;
+  const float* w;
+  uint32_t n;  // T * K
+  int K, E, G, epg;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* slot;
+  int32_t* status;
+  int32_t* gcounts;
+  int32_t* goffsets;
+  int32_t* grow;
+  int32_t* row_src;
+  int32_t* row_idx;
+  float* row_w;
+  int64_t row_cap;
+  int32_t* partials;  // workspace
+};
+hipError_t launch_layout(const LayoutArgs& a, const LayoutGeom& g, hipStream_t s);
+
+struct ScatterArgs {
+  const void* x;
+  void* recv;
+  const int32_t* dest;  // [T*K] slot or grow
+  const int32_t* rows_needed;  // device word
+  int64_t T;
+  int K;
+  int H;
+  int64_t capacity;
+  bool dedup;  // several k may name one row (grouped rows)
+};
+// bf16 rows; `vec_bytes` in {16, 8, 4, 2} divides the row size and both
+// base alignments.
+hipError_t launch_scatter_bf16(const ScatterArgs& a, int vec_bytes, hipStream_t s);
+// packed fp8 rows; H % 128 == 0, 16-byte aligned bases.
+hipError_t launch_scatter_fp8(const ScatterArgs& a, int64_t row_bytes, hipStream_t s);
+
+struct CombineArgs {
+  const void* y;
+  int64_t y_rows;
+  const int32_t* slot;
+  const float* w;
+  const int64_t* idx;  // grouped order only
+  int epg;
+  int E;
+  int64_t T;
+  int K;
+  int H;
+  void* out;
+  int32_t* status;
+  bool grouped;
+};
+// `vec_elems` in {8, 4, 2, 1} divides H and both base alignments (in bf16 elements).
+hipError_t launch_combine(const CombineArgs& a, int vec_elems, hipStream_t s);
+
+}  // namespace ep

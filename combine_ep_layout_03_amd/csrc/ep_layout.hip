@@ -1,0 +1,314 @@
+// Layout kernels: the three dispatch phases of TileScale PR #68 ("EP v2
+// intranode dispatch/combine"; Design section and the commit adding DeepEP's
+// do_expand) on one GPU.
+//   phase 1  k_layout_count   per-block tallies per destination (expert, and
+//                             group when grouped rows are asked for)
+//   phase 2  k_layout_colscan exclusive scan of the tallies over blocks; on
+//                             one GPU the cross-rank count exchange reduces
+//                             to this scan
+//   phase 3  k_layout_place   base + locally claimed slot for every entry
+// The pages claim slots in whatever order lanes arrive; here the claim order
+// is the (t,k) order, so placement is deterministic: inside a wave the rank
+// comes from a match mask built with LDS bit-or (gfx950 has no match-any
+// instruction), across the block's waves from running counters updated wave
+// by wave, across blocks from the scanned tallies.
+#include "ep_device.h"
+#include "ep_internal.h"
+
+namespace ep {
+
+namespace {
+
+// Is (t,k) the first valid entry of token t inside expert group g?  The
+// grouped layout sends one row per (token, group hit); the row is claimed by
+// this entry.
+__device__ __forceinline__ bool first_in_group(const int64_t* __restrict__ idx, uint32_t t, int k,
+                                               int K, int E, int epg, int g) {
+  const int64_t* row = idx + static_cast<size_t>(t) * K;
+  for (int kk = 0; kk < k; ++kk) {
+    const int64_t v = row[kk];
+    if (v >= 0 && v < E && static_cast<int>(v) / epg == g) return false;
+  }
+  return true;
+}
+
+// Exclusive scan of a[0..n) in LDS, n <= 4 * kBlock.  Returns the total.
+// Every thread of the block must call it.
+__device__ int block_exclusive_scan(int* a, int n, int* tmp) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int i0 = tid * 4;
+  int v[4];
+  int s = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v[j] = (i0 + j < n) ? a[i0 + j] : 0;
+    s += v[j];
+  }
+  int x = s;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(x, off, kWave);
+    if (lane >= off) x += y;
+  }
+  if (lane == kWave - 1) tmp[wave] = x;
+  __syncthreads();
+  int before = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < kWavesPerBlock; ++w) {
+    const int t = tmp[w];
+    if (w < wave) before += t;
+    total += t;
+  }
+  int run = before + x - s;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (i0 + j < n) {
+      a[i0 + j] = run;
+      run += v[j];
+    }
+  }
+  __syncthreads();
+  return total;
+}
+
+template <bool GROUPED>
+__global__ __launch_bounds__(kBlock) void k_layout_count(const int64_t* __restrict__ idx,
+                                                         uint32_t n, int K, int E, int epg,
+                                                         int ncols, int rounds,
+                                                         int* __restrict__ partials) {
+  extern __shared__ int cnt[];  // [ncols]
+  for (int c = threadIdx.x; c < ncols; c += kBlock) cnt[c] = 0;
+  __syncthreads();
+  const uint32_t base = blockIdx.x * static_cast<uint32_t>(rounds) * kBlock;
+  for (int r = 0; r < rounds; ++r) {
+    const uint32_t i = base + static_cast<uint32_t>(r) * kBlock + threadIdx.x;
+    if (i >= n) break;
+    const int64_t v = idx[i];
+    if (v >= 0 && v < E) {
+      const int e = static_cast<int>(v);
+      atomicAdd(&cnt[e], 1);
+      if (GROUPED) {
+        const uint32_t t = i / static_cast<uint32_t>(K);
+        const int k = static_cast<int>(i - t * static_cast<uint32_t>(K));
+        const int g = e / epg;
+        if (first_in_group(idx, t, k, K, E, epg, g)) atomicAdd(&cnt[E + g], 1);
+      }
+    } else if (v != -1) {
+      atomicAdd(&cnt[ncols - 1], 1);
+    }
+  }
+  __syncthreads();
+  int* dst = partials + static_cast<size_t>(blockIdx.x) * ncols;
+  for (int c = threadIdx.x; c < ncols; c += kBlock) dst[c] = cnt[c];
+}
+
+// In-place exclusive scan of each column over the nblocks rows; the column
+// totals go to row nblocks.  Block = 64 columns x 16 row slices.
+__global__ __launch_bounds__(1024) void k_layout_colscan(int* __restrict__ partials, int nblocks,
+                                                         int ncols) {
+  __shared__ int s[16][kWave + 1];
+  const int cl = threadIdx.x & (kWave - 1);
+  const int rl = threadIdx.x / kWave;
+  const int c = blockIdx.x * kWave + cl;
+  const int chunk = (nblocks + 15) / 16;
+  const int b0 = min(nblocks, rl * chunk);
+  const int b1 = min(nblocks, b0 + chunk);
+  int sum = 0;
+  if (c < ncols)
+    for (int b = b0; b < b1; ++b) sum += partials[static_cast<size_t>(b) * ncols + c];
+  s[rl][cl] = sum;
+  __syncthreads();
+  if (rl == 0) {
+    int run = 0;
+    for (int j = 0; j < 16; ++j) {
+      const int v = s[j][cl];
+      s[j][cl] = run;
+      run += v;
+    }
+    if (c < ncols) partials[static_cast<size_t>(nblocks) * ncols + c] = run;
+  }
+  __syncthreads();
+  if (c < ncols) {
+    int run = s[rl][cl];
+    for (int b = b0; b < b1; ++b) {
+      const size_t o = static_cast<size_t>(b) * ncols + c;
+      const int v = partials[o];
+      partials[o] = run;
+      run += v;
+    }
+  }
+}
+
+template <bool GROUPED>
+__global__ __launch_bounds__(kBlock) void k_layout_place(LayoutArgs a, int ncols, int rounds,
+                                                         int nblocks) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int E = a.E;
+  const int nkeys = E + (GROUPED ? a.G : 0);
+  uint64_t* bm = reinterpret_cast<uint64_t*>(smem);  // [kWavesPerBlock][nkeys]
+  int* sbase = reinterpret_cast<int*>(bm + kWavesPerBlock * nkeys);  // [nkeys]
+  int* run = sbase + nkeys;                                          // [nkeys]
+  int* tmp = run + nkeys;                                            // [kWavesPerBlock]
+
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int lane = tid & (kWave - 1);
+  const int* tot = a.partials + static_cast<size_t>(nblocks) * ncols;
+
+  // Segment bases: exclusive prefix sums of the totals, over the experts and
+  // (separately) over the groups.
+  for (int c = tid; c < nkeys; c += kBlock) sbase[c] = tot[c];
+  __syncthreads();
+  const int n_sel = block_exclusive_scan(sbase, E, tmp);
+  int n_rows = 0;
+  if (GROUPED) n_rows = block_exclusive_scan(sbase + E, a.G, tmp);
+  const bool lists_ok = !GROUPED || static_cast<int64_t>(n_rows) <= a.row_cap;
+
+  if (blockIdx.x == 0) {
+    for (int e = tid; e < E; e += kBlock) {
+      a.counts[e] = tot[e];
+      a.offsets[e] = sbase[e];
+    }
+    if (GROUPED) {
+      for (int g = tid; g < a.G; g += kBlock) {
+        a.gcounts[g] = tot[E + g];
+        a.goffsets[g] = sbase[E + g];
+      }
+    }
+    if (tid == 0) {
+      a.offsets[E] = n_sel;
+      if (GROUPED) a.goffsets[a.G] = n_rows;
+      a.status[0] = tot[ncols - 1];
+      a.status[1] = n_sel;
+      a.status[2] = n_rows;
+      a.status[3] = lists_ok ? 0 : 1;
+      for (int s = 4; s < 8; ++s) a.status[s] = 0;
+    }
+  }
+
+  // This block's base per key: segment base + entries of earlier blocks.
+  const int* mine = a.partials + static_cast<size_t>(blockIdx.x) * ncols;
+  for (int c = tid; c < nkeys; c += kBlock) {
+    sbase[c] += mine[c];
+    run[c] = 0;
+  }
+  for (int c = tid; c < kWavesPerBlock * nkeys; c += kBlock) bm[c] = 0;
+  __syncthreads();
+
+  uint64_t* wbm = bm + wave * nkeys;
+  const uint64_t bit = 1ull << lane;
+  const uint64_t lt = lanemask_lt();
+  const uint32_t base = blockIdx.x * static_cast<uint32_t>(rounds) * kBlock;
+  for (int r = 0; r < rounds; ++r) {
+    const uint32_t i = base + static_cast<uint32_t>(r) * kBlock + tid;
+    const bool in = i < a.n;
+    const int64_t v = in ? a.idx[i] : -1;
+    const bool valid = in && v >= 0 && v < E;
+    const int e = valid ? static_cast<int>(v) : -1;
+    int kg = -1, g = 0;
+    uint32_t t = 0;
+    if (GROUPED && valid) {
+      t = i / static_cast<uint32_t>(a.K);
+      const int k = static_cast<int>(i - t * static_cast<uint32_t>(a.K));
+      g = e / a.epg;
+      if (first_in_group(a.idx, t, k, a.K, E, a.epg, g)) kg = E + g;
+    }
+    // Lanes of this wave holding the same key: bit-or into the wave's map,
+    // read it back, and let the lowest such lane clear it again.
+    if (e >= 0) atomicOr(reinterpret_cast<unsigned long long*>(&wbm[e]), bit);
+    if (kg >= 0) atomicOr(reinterpret_cast<unsigned long long*>(&wbm[kg]), bit);
+    __syncthreads();
+    const uint64_t mE = e >= 0 ? wbm[e] : 0ull;
+    const uint64_t mG = kg >= 0 ? wbm[kg] : 0ull;
+    __syncthreads();
+    const bool leadE = e >= 0 && (mE & lt) == 0;
+    const bool leadG = kg >= 0 && (mG & lt) == 0;
+    if (leadE) wbm[e] = 0ull;
+    if (leadG) wbm[kg] = 0ull;
+    // Claim slots wave by wave so earlier waves (earlier entries) rank first.
+    int rankE = 0, rankG = 0;
+    for (int w2 = 0; w2 < kWavesPerBlock; ++w2) {
+      __syncthreads();
+      if (wave == w2) {
+        if (e >= 0) rankE = run[e] + __popcll(mE & lt);
+        if (kg >= 0) rankG = run[kg] + __popcll(mG & lt);
+        if (leadE) run[e] = rankE + __popcll(mE);
+        if (leadG) run[kg] = rankG + __popcll(mG);
+      }
+    }
+    if (in) a.slot[i] = e >= 0 ? sbase[e] + rankE : -1;
+    if (GROUPED && in) {
+      if (!valid) a.grow[i] = -1;
+      if (kg >= 0) {
+        const int row = sbase[kg] + rankG;
+        const size_t tk = static_cast<size_t>(t) * a.K;
+        const size_t rk = static_cast<size_t>(row) * a.K;
+        for (int kk = 0; kk < a.K; ++kk) {
+          const int64_t v2 = a.idx[tk + kk];
+          const bool same = v2 >= 0 && v2 < E && static_cast<int>(v2) / a.epg == g;
+          if (same) a.grow[tk + kk] = row;
+          if (lists_ok) {
+            a.row_idx[rk + kk] = same ? static_cast<int>(v2) - g * a.epg : -1;
+            a.row_w[rk + kk] = same ? a.w[tk + kk] : 0.0f;
+          }
+        }
+        if (lists_ok) a.row_src[row] = static_cast<int>(t);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+LayoutGeom layout_geom(int64_t n_entries, int E, int G) {
+  LayoutGeom g;
+  // about 256 blocks at most, each thread taking `rounds` entries
+  const int64_t per_round = static_cast<int64_t>(kBlock) * 256;
+  int64_t rounds = (n_entries + per_round - 1) / per_round;
+  if (rounds < 1) rounds = 1;
+  g.rounds = static_cast<int>(rounds);
+  const int64_t chunk = rounds * kBlock;
+  int64_t nb = (n_entries + chunk - 1) / chunk;
+  if (nb < 1) nb = 1;
+  g.nblocks = static_cast<int>(nb);
+  g.ncols = E + G + 1;
+  return g;
+}
+
+size_t layout_workspace_bytes(const LayoutGeom& g) {
+  const size_t b = static_cast<size_t>(g.nblocks + 1) * g.ncols * sizeof(int32_t);
+  return (b + 255) / 256 * 256;
+}
+
+hipError_t launch_layout(const LayoutArgs& a, const LayoutGeom& geo, hipStream_t s) {
+  const bool grouped = a.G > 0;
+  const size_t count_lds = static_cast<size_t>(geo.ncols) * sizeof(int);
+  if (grouped)
+    k_layout_count<true><<<geo.nblocks, kBlock, count_lds, s>>>(
+        a.idx, a.n, a.K, a.E, a.epg, geo.ncols, geo.rounds, a.partials);
+  else
+    k_layout_count<false><<<geo.nblocks, kBlock, count_lds, s>>>(
+        a.idx, a.n, a.K, a.E, a.epg, geo.ncols, geo.rounds, a.partials);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+
+  k_layout_colscan<<<(geo.ncols + kWave - 1) / kWave, 1024, 0, s>>>(a.partials, geo.nblocks,
+                                                                    geo.ncols);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+
+  const int nkeys = a.E + (grouped ? a.G : 0);
+  const size_t place_lds = static_cast<size_t>(kWavesPerBlock) * nkeys * sizeof(uint64_t) +
+                           static_cast<size_t>(2 * nkeys + kWavesPerBlock) * sizeof(int);
+  if (grouped)
+    k_layout_place<true><<<geo.nblocks, kBlock, place_lds, s>>>(a, geo.ncols, geo.rounds,
+                                                                geo.nblocks);
+  else
+    k_layout_place<false><<<geo.nblocks, kBlock, place_lds, s>>>(a, geo.ncols, geo.rounds,
+                                                                 geo.nblocks);
+  return hipGetLastError();
+}
+
+}  // namespace ep

@@ -1,0 +1,190 @@
+/*
+ * ep_mi355x.h — C ABI of the MoE token dispatch / combine hot path for one
+ * MI355X (gfx950) GPU.
+ *
+ * The operations follow TileScale pull request #68, "[Example] EP v2
+ * intranode dispatch/combine":
+ *   - dispatch counts each token's selections per destination, turns the
+ *     counts into a base per destination, and writes every row straight to
+ *     base + a claimed slot, its final compact index, so no copy epilogue
+ *     runs afterwards (PR summary; PR description, Design section; commit
+ *     adding DeepEP's do_expand, where the destination becomes the expert
+ *     and the base is an exclusive prefix sum of per-expert counts);
+ *   - the fp8 payload is DeepEP's per-token, per-128-element cast, packed
+ *     with its fp32 scales into one row moved by one store (commit packing
+ *     the fp8 payload and scales into one row);
+ *   - topk_idx == -1 means "no selection" and is skipped (commit on masked
+ *     topk_idx);
+ *   - combine gathers each token's expert-output rows and reduces them per
+ *     source token (PR summary; Design section), summing a token's rows
+ *     inside one expert group before the sum across groups (commit adding
+ *     the expanded combine, kDoExpandedSend).
+ *
+ * Conventions for every entry point
+ *   - All device pointers are caller-owned allocations on the current HIP
+ *     device.  The library never allocates, frees or synchronises; every
+ *     call only enqueues kernels on `stream`, and pointers must stay valid
+ *     until the stream reaches that work.
+ *   - Inputs are read-only.  Outputs are fully overwritten as documented.
+ *   - Host-checkable errors return a nonzero code before anything is
+ *     enqueued.  Data-dependent conditions are reported in the device
+ *     status words (EP_STATUS_*), never by corrupting memory.
+ *   - bf16 values are 16-bit IEEE-style bfloat16 bit patterns; fp32 is IEEE
+ *     binary32; all integers are little-endian.
+ */
+#ifndef EP_MI355X_H
+#define EP_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- return codes ---------------------------------------------------- */
+#define EP_OK 0
+#define EP_EINVAL 1     /* null pointer, bad size, misaligned base pointer */
+#define EP_ENOTSUP 2    /* valid but unsupported (fp8 with hidden % 128 != 0, limits) */
+#define EP_EHIP 3       /* a HIP launch failed (hipGetLastError) */
+#define EP_EWORKSPACE 4 /* workspace smaller than ep_layout_workspace_bytes() */
+
+/* ---- limits ---------------------------------------------------------- */
+#define EP_MAX_TOPK 32     /* K */
+#define EP_MAX_KEYS 1024   /* E + G (destinations counted by the layout) */
+
+/* ---- device status words written by ep_layout ------------------------ */
+#define EP_STATUS_INVALID_IDS 0 /* ids outside {-1} U [0,E): counted, treated as -1 */
+#define EP_STATUS_ROWS_EXPERT 1 /* N_sel: rows of the expert-major layout */
+#define EP_STATUS_ROWS_GROUP 2  /* R: rows of the grouped layout (0 without groups) */
+#define EP_STATUS_LIST_OVERFLOW 3 /* 1 if R > row_capacity: row lists not written */
+#define EP_STATUS_COMBINE_OOB 4 /* set to 1 by ep_combine if a slot >= y_rows was met */
+#define EP_STATUS_WORDS 8
+
+/* ---- formats, row kinds, combine orders ------------------------------ */
+#define EP_FORMAT_BF16 0       /* receive row = the token's H bf16 values */
+#define EP_FORMAT_FP8_PACKED 1 /* receive row = ep_fp8_row_bytes(H) bytes */
+
+#define EP_ROWS_EXPERT 0 /* one row per valid (token, k), expert-major */
+#define EP_ROWS_GROUP 1  /* one row per (token, group hit), group-major */
+
+#define EP_COMBINE_FLAT 0    /* ascending k */
+#define EP_COMBINE_GROUPED 1 /* within each group ascending k, then groups ascending */
+
+/* Problem shape.
+ *   num_tokens  T >= 0 source tokens
+ *   hidden      H >= 1 elements per token row
+ *   topk        K in [1, EP_MAX_TOPK]
+ *   num_experts E >= 1
+ *   num_groups  G: 0 = expert-major layout only; G >= 1 dividing E = the E
+ *               experts also form G contiguous groups of E/G (a group plays
+ *               the role of a destination rank) and the layout adds one
+ *               deduplicated row per (token, group hit).  E + G must not
+ *               exceed EP_MAX_KEYS. */
+typedef struct ep_problem {
+  int64_t num_tokens;
+  int32_t hidden;
+  int32_t topk;
+  int32_t num_experts;
+  int32_t num_groups;
+} ep_problem_t;
+
+/* Layout outputs: device pointers, caller-owned, all int32 unless noted.
+ *   counts[E]          selections per expert
+ *   offsets[E+1]       exclusive prefix sum of counts; offsets[E] = N_sel
+ *   slot[T*K]          expert-major row of (t,k): offsets[e] + number of
+ *                      earlier (t',k') in (t,k) order with the same expert;
+ *                      -1 for masked or invalid entries
+ *   status[EP_STATUS_WORDS]
+ * Grouped layout (only read/written when num_groups >= 1; may be NULL otherwise):
+ *   group_counts[G], group_offsets[G+1]   rows per group and their prefix sum
+ *   grow[T*K]          grouped row carrying (t,k): group_offsets[g] + number
+ *                      of tokens t' < t hitting group g; -1 if masked
+ *   row_src[row_capacity]                 source token of each grouped row
+ *   row_topk_idx[row_capacity*K]          per row, per k: the expert's index
+ *                      inside the row's group if (t,k) is valid and in that
+ *                      group, else -1
+ *   row_topk_weights[row_capacity*K]      fp32: topk_weights[t,k] under the
+ *                      same condition, else 0
+ *   row_capacity       rows the three lists hold; if R exceeds it the lists
+ *                      are not written and EP_STATUS_LIST_OVERFLOW is set. */
+typedef struct ep_layout {
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* slot;
+  int32_t* status;
+  int32_t* group_counts;
+  int32_t* group_offsets;
+  int32_t* grow;
+  int32_t* row_src;
+  int32_t* row_topk_idx;
+  float* row_topk_weights;
+  int64_t row_capacity;
+} ep_layout_t;
+
+/* Bytes of one packed fp8 row: H bytes of E4M3FN payload, then H/128
+ * little-endian fp32 scales, zero-padded to a multiple of 16 bytes
+ * (hidden 7168 -> 7392, hidden 128 -> 144).  Returns -1 if hidden <= 0 or
+ * hidden % 128 != 0.  Host only; no device work. */
+int64_t ep_fp8_row_bytes(int32_t hidden);
+
+/* Bytes of device workspace ep_layout needs for this problem (per-block
+ * partial counts).  Returns 0 for an invalid problem.  Host only. */
+size_t ep_layout_workspace_bytes(const ep_problem_t* p);
+
+/* Layout: phase 1 (count per expert, and per group), phase 2 (exclusive
+ * scan into bases) and phase 3 (slots and grouped rows) for topk_idx int64
+ * [T*K] row-major.  topk_weights fp32 [T*K] is read only to fill
+ * row_topk_weights and may be NULL when num_groups == 0.  `workspace` must
+ * hold ep_layout_workspace_bytes(p) bytes (contents need no initialisation
+ * and are clobbered).  Writes every output of `L` listed above, including
+ * all status words except EP_STATUS_COMBINE_OOB, which it clears.
+ * Placement is deterministic: identical inputs give identical bytes. */
+int ep_layout(const ep_problem_t* p, const int64_t* topk_idx, const float* topk_weights,
+              const ep_layout_t* L, void* workspace, size_t workspace_bytes,
+              hipStream_t stream);
+
+/* Dispatch: scatter every token row of x (bf16 [T*H]) to the receive rows
+ * the layout assigned it.
+ *   rows == EP_ROWS_EXPERT: recv row slot[t,k] for each valid (t,k);
+ *   rows == EP_ROWS_GROUP:  recv row grow[t,k] once per distinct row.
+ *   format == EP_FORMAT_BF16:       recv is bf16 [capacity_rows * H];
+ *   format == EP_FORMAT_FP8_PACKED: recv is uint8 [capacity_rows * ep_fp8_row_bytes(H)],
+ *     each row quantised per 128-element group j as s_j = amax_j / 448 and
+ *     q = E4M3FN(x / s_j) (both fp32 IEEE divisions, round to nearest even,
+ *     saturating at 448; s_j == 0 gives q = 0), requires H % 128 == 0.
+ * Each source row is read once and written once per destination row.  If
+ * the rows needed (status word EP_STATUS_ROWS_EXPERT or _GROUP) exceed
+ * capacity_rows the call writes nothing: an overflow is known before any
+ * payload moves.  Rows at or beyond the rows needed are never touched.
+ * Base pointers of x and recv must be 16-byte aligned for the fp8 format;
+ * for bf16 any 2-byte alignment works (wider alignment is faster). */
+int ep_dispatch(const ep_problem_t* p, const ep_layout_t* L, const void* x, void* recv,
+                int64_t capacity_rows, int32_t rows, int32_t format, hipStream_t stream);
+
+/* Combine: out[t] (bf16 [T*H]) = bf16_rne of the fp32 sum over the token's
+ * valid selections of topk_weights[t,k] * y[slot[t,k]], with y bf16
+ * [y_rows * H] in expert-major receive order (y row r is the expert output
+ * for receive row r).  Each product and each sum is one fp32 rounding (no
+ * fused multiply-add); accumulation starts from +0.
+ *   order == EP_COMBINE_FLAT:    ascending k;
+ *   order == EP_COMBINE_GROUPED: per group in ascending k, then the group
+ *     partials in ascending group order (needs num_groups >= 1 and
+ *     topk_idx int64 [T*K]; topk_idx may be NULL for the flat order).
+ * A token with no valid selection gives +0 everywhere.  A slot >= y_rows
+ * is skipped and sets status word EP_STATUS_COMBINE_OOB.  Every one of the
+ * T output rows is written. */
+int ep_combine(const ep_problem_t* p, const ep_layout_t* L, const int64_t* topk_idx,
+               const float* topk_weights, const void* y, int64_t y_rows, void* out,
+               int32_t order, hipStream_t stream);
+
+/* Static description of a return code. */
+const char* ep_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EP_MI355X_H */

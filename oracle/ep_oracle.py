@@ -304,10 +304,10 @@ def quantize_row_fp8(x_row_u16) -> np.ndarray:
     a = np.max(np.abs(xf), axis=1).astype(np.float32)
     s = (a / np.float32(FP8_MAX)).astype(np.float32)
     q = np.zeros((H // FP8_GROUP, FP8_GROUP), dtype=np.uint8)
-    for j in range(H // FP8_GROUP):
-        if s[j] != 0:
-            v = (xf[j] / s[j]).astype(np.float32)
-            q[j] = e4m3fn_rne_sat(v)
+    nz = s != 0
+    if nz.any():
+        v = (xf[nz] / s[nz][:, None]).astype(np.float32)
+        q[nz] = e4m3fn_rne_sat(v)
     row = np.zeros(rb, dtype=np.uint8)
     row[:H] = q.reshape(-1)
     row[H : H + 4 * (H // FP8_GROUP)] = s.astype("<f4").view(np.uint8)

@@ -1,0 +1,90 @@
+"""The C-ABI library loads and exports every symbol include/ep_mi355x.h declares
+(CPU only: no call here launches device work)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ep_mi355x.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ep_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    assert _declared() == sorted(
+        ["ep_fp8_row_bytes", "ep_layout_workspace_bytes", "ep_layout", "ep_dispatch", "ep_combine", "ep_strerror"]
+    )
+
+
+def test_library_exports_every_declared_symbol():
+    from combine_ep_layout_03_amd import _lib
+
+    L = _lib.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+        assert name in _lib.EXPORTS
+
+
+def test_host_only_entry_points():
+    import combine_ep_layout_03_amd as ep
+
+    assert ep.ep_fp8_row_bytes(7168) == 7392
+    assert ep.ep_fp8_row_bytes(128) == 144
+    assert ep.ep_fp8_row_bytes(2048) == 2112
+    assert ep.ep_fp8_row_bytes(100) == -1
+    assert ep.ep_fp8_row_bytes(0) == -1
+    assert ep.ep_layout_workspace_bytes(8192, 8, 256) > 0
+    assert ep.ep_layout_workspace_bytes(8192, 8, 256, 8) > ep.ep_layout_workspace_bytes(8192, 8, 256)
+    assert ep.ep_layout_workspace_bytes(0, 8, 256) > 0  # T = 0 still publishes counts
+    assert ep.ep_layout_workspace_bytes(10, 8, 256, 7) == 0  # G must divide E
+    assert ep.ep_layout_workspace_bytes(10, 33, 256) == 0  # K above the limit
+    assert ep.ep_layout_workspace_bytes(10, 8, 1024, 8) == 0  # E + G above the limit
+    for c in range(5):
+        assert ep.ep_strerror(c)
+
+
+def test_invalid_arguments_return_codes_before_any_launch():
+    """Host checks reject bad calls without touching a device (null pointers)."""
+    from combine_ep_layout_03_amd import _lib
+
+    L = _lib.lib()
+    p = _lib.Problem(16, 256, 8, 256, 0)
+    lay = _lib.LayoutStruct()
+    # null layout outputs
+    assert L.ep_layout(ctypes.byref(p), None, None, ctypes.byref(lay), None, 0, None) == _lib.EP_EINVAL
+    # bad shapes
+    bad = _lib.Problem(16, 256, 0, 256, 0)
+    assert L.ep_dispatch(ctypes.byref(bad), ctypes.byref(lay), None, None, 0, 0, 0, None) == _lib.EP_EINVAL
+    bad = _lib.Problem(16, 256, 8, 256, 3)
+    assert L.ep_combine(ctypes.byref(bad), ctypes.byref(lay), None, None, None, 0, None, 0, None) == _lib.EP_EINVAL
+    # fp8 with hidden % 128 != 0 is unsupported (checked before pointers)
+    p2 = _lib.Problem(16, 100, 8, 256, 0)
+    lay.status = 8  # any non-null value; never dereferenced on this path
+    assert (
+        L.ep_dispatch(ctypes.byref(p2), ctypes.byref(lay), None, None, 0, _lib.EP_ROWS_EXPERT, _lib.EP_FORMAT_FP8_PACKED, None)
+        == _lib.EP_ENOTSUP
+    )
+    # grouped rows without groups
+    assert (
+        L.ep_dispatch(ctypes.byref(p), ctypes.byref(lay), None, None, 0, _lib.EP_ROWS_GROUP, _lib.EP_FORMAT_BF16, None)
+        == _lib.EP_EINVAL
+    )
+    # T = 0 dispatch / combine are valid no-ops that launch nothing
+    p0 = _lib.Problem(0, 256, 8, 256, 0)
+    assert L.ep_dispatch(ctypes.byref(p0), ctypes.byref(lay), None, None, 0, 0, 0, None) == _lib.EP_OK
+    assert L.ep_combine(ctypes.byref(p0), ctypes.byref(lay), None, None, None, 0, None, 0, None) == _lib.EP_OK
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+
+    import combine_ep_layout_03_amd as ep
+
+    with pytest.raises(ValueError):
+        ep.ep_layout(torch.zeros(4, 2, dtype=torch.int64), 8)

@@ -1,0 +1,414 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Integer layouts, row placement, bf16 rows, fp8 payload/scale bytes and the
+bf16 combine output are compared bit for bit: the combine's fp32 order is
+fixed, so its tolerance is zero.  Small cases are compared in full; the
+workload shapes are compared in full where the oracle finishes in seconds
+and on sampled rows / tokens otherwise (the grouped 65536-token case).
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import ep_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import combine_ep_layout_03_amd as ep  # noqa: F401  (fails loudly if not built)
+
+    torch.cuda.init()
+    yield
+    torch.cuda.synchronize()
+
+
+def ep():
+    import combine_ep_layout_03_amd as m
+
+    return m
+
+
+def u16(t: torch.Tensor) -> np.ndarray:
+    return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def check_layout(L, R, E, G=0):
+    torch.cuda.synchronize()
+    assert np.array_equal(L.counts.cpu().numpy(), R["counts"])
+    assert np.array_equal(L.offsets.cpu().numpy(), R["offsets"])
+    assert np.array_equal(L.slot.cpu().numpy(), R["slot"])
+    st = L.status.cpu().numpy()
+    assert st[0] == R["n_invalid"] and st[1] == R["n_sel"]
+    if G:
+        assert st[2] == R["n_rows"]
+        assert np.array_equal(L.group_counts.cpu().numpy(), R["gcounts"])
+        assert np.array_equal(L.group_offsets.cpu().numpy(), R["goffsets"])
+        assert np.array_equal(L.grow.cpu().numpy(), R["grow"])
+        if st[3] == 0:
+            n = R["n_rows"]
+            assert np.array_equal(L.row_src[:n].cpu().numpy(), R["src"])
+            assert np.array_equal(L.row_topk_idx[:n].cpu().numpy(), R["ridx"])
+            assert np.array_equal(L.row_topk_weights[:n].cpu().numpy().view(np.uint32), R["rw"].view(np.uint32))
+    else:
+        assert st[2] == 0
+
+
+# --------------------------------------------------------------------------- layout
+@pytest.mark.parametrize("name", ["tiny", "mid", "pages", "skewed_masked", "grouped"])
+def test_layout_workloads(name):
+    w = W.by_name(name)
+    say("layout", name, w.T, w.K, w.E, w.G)
+    idx, wt = W.make_routing(w)
+    G = w.G if w.G > 1 else 0
+    R = O.layout(idx.numpy(), w.E, G, wt.numpy())
+    L = ep().ep_layout(idx.to(DEV), w.E, G, wt.to(DEV) if G else None)
+    check_layout(L, R, w.E, G)
+
+
+@pytest.mark.parametrize(
+    "T,K,E,G,mask",
+    [
+        (0, 8, 256, 0, 0.0),
+        (0, 8, 256, 8, 0.0),
+        (1, 1, 1, 0, 0.0),
+        (5, 3, 7, 0, 0.3),
+        (777, 6, 96, 0, 0.2),  # K does not divide a wave; ragged last block
+        (1000, 8, 64, 1, 0.1),  # one group: one row per active token
+        (1000, 8, 64, 64, 0.1),  # a group per expert
+        (513, 5, 40, 8, 0.25),
+        (20000, 8, 256, 8, 0.05),  # several rounds per block
+        (3000, 32, 512, 16, 0.0),  # K at the limit
+        (2000, 4, 1000, 0, 0.0),  # E near the key limit
+    ],
+)
+def test_layout_edge_shapes(T, K, E, G, mask):
+    say("layout edge", T, K, E, G, mask)
+    w = W.Workload("edge", T=T, H=8, K=K, E=E, G=max(G, 1), mask_p=mask, seed=T + K + E)
+    if T:
+        idx, wt = W.make_routing(w)
+    else:
+        idx, wt = torch.zeros(0, K, dtype=torch.int64), torch.zeros(0, K)
+    R = O.layout(idx.numpy(), E, G, wt.numpy())
+    L = ep().ep_layout(idx.to(DEV), E, G, wt.to(DEV) if G else None)
+    check_layout(L, R, E, G)
+
+
+def test_layout_invalid_and_duplicate_ids():
+    g = torch.Generator().manual_seed(11)
+    T, K, E = 3000, 8, 64
+    idx = torch.randint(-3, E + 3, (T, K), generator=g)  # -3,-2,E.. invalid; duplicates allowed
+    wt = torch.rand(T, K, generator=g)
+    for G in (0, 8):
+        R = O.layout(idx.numpy(), E, G, wt.numpy())
+        L = ep().ep_layout(idx.to(DEV), E, G, wt.to(DEV) if G else None)
+        check_layout(L, R, E, G)
+        assert R["n_invalid"] > 0
+
+
+def test_layout_list_overflow_reported():
+    w = W.by_name("grouped").replace(T=4000)
+    idx, wt = W.make_routing(w)
+    R = O.layout(idx.numpy(), w.E, w.G, wt.numpy())
+    L = ep().ep_layout(idx.to(DEV), w.E, w.G, wt.to(DEV), row_capacity=R["n_rows"] - 1)
+    torch.cuda.synchronize()
+    assert L.status[3].item() == 1
+    assert np.array_equal(L.grow.cpu().numpy(), R["grow"])
+
+
+def test_layout_repeat_bit_identical():
+    w = W.by_name("skewed_masked")
+    idx, wt = W.make_routing(w)
+    d_idx, d_wt = idx.to(DEV), wt.to(DEV)
+    L0 = ep().ep_layout(d_idx, w.E, 8, d_wt)
+    n = L0.num_rows(ep().EP_ROWS_GROUP)
+
+    def outs(L):
+        # row lists hold n rows; the rest of their capacity is never written
+        return (L.slot, L.grow, L.row_src[:n], L.row_topk_idx[:n], L.row_topk_weights[:n], L.status)
+
+    ref = [t.clone() for t in outs(L0)]
+    for _ in range(200):
+        L = ep().ep_layout(d_idx, w.E, 8, d_wt)
+        for a, b in zip(ref, outs(L)):
+            assert torch.equal(a, b)
+
+
+# --------------------------------------------------------------------------- dispatch
+def _dispatch_case(w, fp8=False, x=None, x_offset=0):
+    idx, wt = W.make_routing(w)
+    if x is None:
+        x = W.make_x(w)
+    R = O.layout(idx.numpy(), w.E)
+    L = ep().ep_layout(idx.to(DEV), w.E)
+    if x_offset:
+        buf = torch.empty(w.T * w.H + x_offset, dtype=torch.bfloat16, device=DEV)
+        xd = buf[x_offset:].view(w.T, w.H)
+        xd.copy_(x)
+    else:
+        xd = x.to(DEV)
+    recv = ep().ep_dispatch(xd, L, fp8=fp8)
+    n = R["n_sel"]
+    xr = u16(x)
+    if fp8:
+        want = O.dispatch_fp8(xr, R["slot"], n)
+        got = recv[:n].cpu().numpy()
+    else:
+        want = O.dispatch_bf16(xr, R["slot"], n)
+        got = u16(recv[:n])
+    assert got.shape == want.shape
+    assert np.array_equal(got, want)
+    return L, R, recv
+
+
+@pytest.mark.parametrize("H", [1, 2, 3, 5, 7, 8, 9, 127, 129, 136, 7168])
+def test_dispatch_bf16_tails(H):
+    say("dispatch bf16 H", H)
+    _dispatch_case(W.Workload("tail", T=300, H=H, K=4, E=16, mask_p=0.1, seed=H))
+
+
+@pytest.mark.parametrize("off", [1, 2, 4])
+def test_dispatch_bf16_misaligned_base(off):
+    _dispatch_case(W.Workload("mis", T=200, H=64, K=3, E=10, seed=off), x_offset=off)
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid", "skewed_masked"])
+def test_dispatch_bf16_workloads(name):
+    say("dispatch bf16", name)
+    _dispatch_case(W.by_name(name))
+
+
+def test_dispatch_bf16_pages_shape():
+    say("dispatch bf16 pages shape")
+    _dispatch_case(W.by_name("pages").replace(fp8=False))
+
+
+def test_dispatch_fp8_pages_shape():
+    say("dispatch fp8 pages shape")
+    _dispatch_case(W.by_name("pages"), fp8=True)
+
+
+@pytest.mark.parametrize("H", [128, 256, 1152, 2048])
+def test_dispatch_fp8_small_hidden(H):
+    _dispatch_case(W.Workload("fp8h", T=257, H=H, K=4, E=32, mask_p=0.1, seed=H), fp8=True)
+
+
+def _special_fp8_rows(H=1024):
+    """Rows that exercise every corner of the packed fp8 cast.
+
+    Groups: all zeros; one group per bf16 bit pattern block with a 448
+    element (scale exactly 1, so the payload is the E4M3FN code of the bf16
+    value itself: together the rows cover every finite bf16 of magnitude
+    <= 448); tiny values whose scale is subnormal; -0.0; values exactly on
+    E4M3FN midpoints."""
+    rows = []
+    allb = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    f = O.bf16_to_f32(allb)
+    keep = allb[np.isfinite(f) & (np.abs(f) <= 448.0)]
+    per = 127
+    b448 = O.bf16_rne(np.array([448.0], np.float32))[0]
+    groups = []
+    for i in range(0, len(keep), per):
+        g = np.full(128, b448, np.uint16)
+        chunk = keep[i : i + per]
+        g[1 : 1 + len(chunk)] = chunk
+        groups.append(g)
+    groups.append(np.zeros(128, np.uint16))  # scale 0
+    groups.append(np.full(128, 0x8000, np.uint16))  # -0.0
+    tiny = O.bf16_rne(np.linspace(-1e-38, 1e-38, 128).astype(np.float32))
+    groups.append(tiny)  # subnormal scale
+    t = O.e4m3fn_value_table()
+    mids = O.bf16_rne(((t[:-1] + t[1:]) / 2).astype(np.float32))
+    g = np.full(128, b448, np.uint16)
+    g[1 : 1 + len(mids)] = mids
+    groups.append(g)
+    flat = np.concatenate(groups)
+    pad = (-len(flat)) % H
+    flat = np.concatenate([flat, np.zeros(pad, np.uint16)])
+    return flat.reshape(-1, H)
+
+
+def test_dispatch_fp8_special_values():
+    xs = _special_fp8_rows()
+    T, H = xs.shape
+    w = W.Workload("fp8s", T=T, H=H, K=2, E=4)
+    x = torch.from_numpy(xs.view(np.int16)).view(torch.bfloat16)
+    _dispatch_case(w, fp8=True, x=x)
+
+
+def test_dispatch_poison_and_capacity():
+    w = W.by_name("skewed_masked").replace(T=1500, H=520)
+    idx, _ = W.make_routing(w)
+    x = W.make_x(w).to(DEV)
+    L = ep().ep_layout(idx.to(DEV), w.E)
+    n = L.num_rows()
+    cap = w.T * w.K
+    out = torch.full((cap, w.H), -1, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    ep().ep_dispatch(x, L, out=out)
+    torch.cuda.synchronize()
+    tail = out[n:].view(torch.int16)
+    assert bool((tail == -1).all()), "rows past N_sel were written"
+    assert not bool((out[:n].view(torch.int16) == -1).all(dim=1).any()), "a row below N_sel was not written"
+    # capacity below the rows needed: nothing is written at all
+    out2 = torch.full((n - 1, w.H), -1, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    ep().ep_dispatch(x, L, capacity=n - 1, out=out2)
+    rb = ep().ep_fp8_row_bytes(512)
+    out3 = torch.full((n - 1, rb), 0xAB, dtype=torch.uint8, device=DEV)
+    w2 = w.replace(H=512)
+    ep().ep_dispatch(W.make_x(w2).to(DEV), L, fp8=True, capacity=n - 1, out=out3)
+    torch.cuda.synchronize()
+    assert bool((out2.view(torch.int16) == -1).all())
+    assert bool((out3 == 0xAB).all())
+
+
+def test_dispatch_grouped_rows_small():
+    w = W.by_name("grouped").replace(T=3000, H=264, mask_p=0.1)
+    idx, wt = W.make_routing(w)
+    x = W.make_x(w)
+    R = O.layout(idx.numpy(), w.E, w.G, wt.numpy())
+    L = ep().ep_layout(idx.to(DEV), w.E, w.G, wt.to(DEV))
+    recv = ep().ep_dispatch(x.to(DEV), L, rows=ep().EP_ROWS_GROUP)
+    n = R["n_rows"]
+    assert np.array_equal(u16(recv[:n]), O.dispatch_bf16(u16(x), R["grow"], n))
+    w8 = w.replace(H=256)
+    x8 = W.make_x(w8)
+    recv8 = ep().ep_dispatch(x8.to(DEV), L, fp8=True, rows=ep().EP_ROWS_GROUP)
+    assert np.array_equal(recv8[:n].cpu().numpy(), O.dispatch_fp8(u16(x8), R["grow"], n))
+
+
+def test_dispatch_repeat_bit_identical():
+    w = W.by_name("mid")
+    idx, _ = W.make_routing(w)
+    x = W.make_x(w).to(DEV)
+    L = ep().ep_layout(idx.to(DEV), w.E)
+    ref = ep().ep_dispatch(x, L).clone()
+    out = torch.empty_like(ref)
+    for _ in range(100):
+        ep().ep_dispatch(x, L, out=out)
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
+# --------------------------------------------------------------------------- combine
+def _combine_case(w, y=None, grouped=False, G=0):
+    idx, wt = W.make_routing(w)
+    R = O.layout(idx.numpy(), w.E, G, wt.numpy())
+    L = ep().ep_layout(idx.to(DEV), w.E, G, wt.to(DEV) if G else None)
+    if y is None:
+        y = W.make_y(w, rows=max(R["n_sel"], 1))
+    order = ep().EP_COMBINE_GROUPED if grouped else ep().EP_COMBINE_FLAT
+    out = ep().ep_combine(y.to(DEV), L, wt.to(DEV), idx.to(DEV), order=order)
+    yr = u16(y)
+    if grouped:
+        want = O.combine_grouped(yr, idx.numpy(), R["slot"], wt.numpy(), w.E, G)
+    else:
+        want = O.combine(yr, R["slot"], wt.numpy())
+    got = u16(out)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:5].tolist()}"
+    return out
+
+
+def test_combine_tiny_scaled_rows():
+    w = W.by_name("tiny")
+    idx, wt = W.make_routing(w)
+    x = W.make_x(w)
+    R = O.layout(idx.numpy(), w.E)
+    L = ep().ep_layout(idx.to(DEV), w.E)
+    recv = ep().ep_dispatch(x.to(DEV), L)[: R["n_sel"]]
+    row_e = np.searchsorted(R["offsets"], np.arange(R["n_sel"]), side="right") - 1
+    y = W.tiny_expert_outputs(recv.cpu(), torch.from_numpy(row_e))
+    out = ep().ep_combine(y.to(DEV), L, wt.to(DEV))
+    assert np.array_equal(u16(out), O.combine(u16(y), R["slot"], wt.numpy()))
+
+
+@pytest.mark.parametrize("H", [1, 3, 5, 8, 9, 129, 7168])
+def test_combine_tails(H):
+    say("combine H", H)
+    _combine_case(W.Workload("ctail", T=300, H=H, K=4, E=16, mask_p=0.2, seed=H))
+
+
+@pytest.mark.parametrize("K", [1, 2, 3, 8, 13, 32])
+def test_combine_topk_range(K):
+    _combine_case(W.Workload("ck", T=200, H=64, K=K, E=64, mask_p=0.1, seed=K))
+
+
+@pytest.mark.parametrize("name", ["mid", "skewed_masked"])
+def test_combine_workloads(name):
+    say("combine", name)
+    _combine_case(W.by_name(name))
+
+
+def test_combine_pages_shape():
+    say("combine pages shape")
+    _combine_case(W.by_name("pages"))
+
+
+@pytest.mark.parametrize("G", [1, 2, 8, 64])
+def test_combine_grouped_small(G):
+    _combine_case(W.Workload("cg", T=500, H=136, K=8, E=64, mask_p=0.15, seed=G), grouped=True, G=G)
+
+
+def test_combine_fully_masked_and_oob():
+    w = W.Workload("cm", T=64, H=32, K=4, E=8)
+    idx, wt = W.make_routing(w)
+    idx[5] = -1
+    idx[9] = -1
+    L = ep().ep_layout(idx.to(DEV), w.E)
+    n = L.num_rows()
+    y = W.make_y(w, rows=n).to(DEV)
+    out = ep().ep_combine(y, L, wt.to(DEV))
+    torch.cuda.synchronize()
+    assert bool((out[5].view(torch.int16) == 0).all()) and bool((out[9].view(torch.int16) == 0).all())
+    assert L.status[ep().EP_STATUS_COMBINE_OOB].item() == 0
+    # y shorter than the rows the layout needs: those rows are skipped and reported
+    ep().ep_combine(y[: n // 2], L, wt.to(DEV))
+    torch.cuda.synchronize()
+    assert L.status[ep().EP_STATUS_COMBINE_OOB].item() == 1
+
+
+# --------------------------------------------------------------------------- grouped workload
+def test_grouped_workload_sampled():
+    """65536 tokens, 8 groups of 32 experts: layout in full, grouped dispatch
+    and grouped combine on sampled rows and tokens."""
+    w = W.by_name("grouped")
+    say("grouped workload: inputs")
+    idx, wt = W.make_routing(w)
+    R = O.layout(idx.numpy(), w.E, w.G, wt.numpy())
+    x = W.make_x(w, device=DEV)
+    d_idx, d_wt = idx.to(DEV), wt.to(DEV)
+    L = ep().ep_layout(d_idx, w.E, w.G, d_wt)
+    check_layout(L, R, w.E, w.G)
+    say("grouped workload: dispatch")
+    recv = ep().ep_dispatch(x, L, rows=ep().EP_ROWS_GROUP)
+    n = R["n_rows"]
+    gen = np.random.default_rng(0)
+    rows = np.concatenate([[0, n - 1], gen.choice(n, 3000, replace=False)])
+    rsel = torch.from_numpy(rows).to(DEV)
+    got = u16(recv.index_select(0, rsel))
+    src = torch.from_numpy(R["src"][rows]).to(DEV)
+    want = u16(x.index_select(0, src))
+    assert np.array_equal(got, want)
+    del recv
+    say("grouped workload: combine")
+    y = W.make_y(w, device=DEV)
+    out = ep().ep_combine(y, L, d_wt, d_idx, order=ep().EP_COMBINE_GROUPED)
+    toks = np.concatenate([[0, w.T - 1], gen.choice(w.T, 600, replace=False)])
+    slot_s = R["slot"][toks]
+    used = np.unique(slot_s[slot_s >= 0])
+    remap = -np.ones(R["n_sel"] + 1, np.int64)
+    remap[used] = np.arange(len(used))
+    slot_r = np.where(slot_s >= 0, remap[np.maximum(slot_s, 0)], -1)
+    ysub = u16(y.index_select(0, torch.from_numpy(used).to(DEV)))
+    want = O.combine_grouped(ysub, idx.numpy()[toks], slot_r, wt.numpy()[toks], w.E, w.G)
+    got = u16(out.index_select(0, torch.from_numpy(toks).to(DEV)))
+    assert np.array_equal(got, want)

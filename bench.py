@@ -89,6 +89,11 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
     ap.add_argument("--bf16-dispatch", action="store_true", help="also time the bf16 dispatch variant")
+    ap.add_argument(
+        "--isolated",
+        action="store_true",
+        help="also time each op alone, back to back, outside the step (diagnostic)",
+    )
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(
@@ -191,6 +196,26 @@ def main(argv=None):
     }
     if t_bf16:
         ops["dispatch_bf16"] = stats(t_bf16, nb["dispatch_bf16"])
+    if args.isolated:
+        iso = {
+            "layout": lambda: ep.ep_layout(d_idx, E, out=L),
+            "dispatch_fp8": lambda: ep.ep_dispatch(x, L, fp8=True, out=recv8),
+            "combine": lambda: ep.ep_combine(y, L, d_wt, out=out),
+        }
+        if recv16 is not None:
+            iso["dispatch_bf16"] = lambda: ep.ep_dispatch(x, L, fp8=False, out=recv16)
+        for name, fn in iso.items():
+            fn()
+            a0 = torch.cuda.Event(enable_timing=True)
+            a1 = torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
+            for _ in range(args.steps):
+                fn()
+            a1.record(stream)
+            torch.cuda.synchronize()
+            us = a0.elapsed_time(a1) * 1e3 / args.steps
+            ops[name]["isolated_us"] = round(us, 2)
+            ops[name]["isolated_GBps"] = round(nb[name] / (us * 1e-6) / 1e9, 1)
     step_bytes = nb["layout"] + nb["dispatch_fp8"] + nb["combine"]
     step_ms = statistics.median(t_step)
     value = step_bytes / (step_ms * 1e-3) / 1e9

@@ -1,8 +1,7 @@
-// Combine: one wave per source token gathers the token's expert-output rows
-// and reduces them, the one-block-per-source-token local reduce of TileScale
-// PR #68 (PR summary; Design section).  Rows are found through the forward
-// map slot[t,k] the layout wrote, so no inverse bucketing is needed on one
-// GPU.
+// Combine: gather each source token's expert-output rows and reduce them,
+// the one-block-per-source-token local reduce of TileScale PR #68 (PR
+// summary; Design section).  Rows are found through the forward map
+// slot[t,k] the layout wrote, so no inverse bucketing is needed on one GPU.
 //
 // Arithmetic (exactly what the reduction order defines, no fused
 // multiply-add): acc starts at +0, each term is fl32(w * y) and each sum is
@@ -12,10 +11,17 @@
 // token's local-expert rows before one row per destination is sent (commit
 // adding kDoExpandedSend).  Masked entries (-1) are skipped, so a fully
 // masked token gives +0 (commit on masked topk_idx).
+//
+// Work split: a token row is cut into chunks of 64*U vectors; the
+// persistent grid's waves take contiguous ranges of (token, chunk) items, so
+// the load is balanced to within one chunk and a wave reloads the token's
+// selection list only when it moves to the next token.  Expert-output rows
+// are read exactly once, with non-temporal loads.
 #include <limits.h>
 
 #include "ep_device.h"
 #include "ep_internal.h"
+#include "ep_launch.h"
 
 namespace ep {
 
@@ -64,17 +70,18 @@ struct BfVec<1> {
   }
 };
 
-template <int KMAX, int VE, bool GROUPED, int U>
-__global__ __launch_bounds__(kBlock) void k_combine(CombineArgs a) {
-  using B = BfVec<VE>;
-  using V = typename B::V;
-  const int wave = threadIdx.x / kWave;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave;
-  if (t >= a.T) return;
-  const int K = a.K;
+// A token's valid selections in summation order, wave-uniform.
+template <int KMAX>
+struct Sel {
+  int nv;           // number of valid selections
+  int os[KMAX];     // receive rows; entries past nv repeat the first row
+  float ow[KMAX];   // weights
+  bool newg[KMAX];  // position i starts a new group (never position 0)
+};
 
-  // Per-lane selection k = lane.
+template <int KMAX, bool GROUPED>
+__device__ __forceinline__ void load_sel(const CombineArgs& a, int64_t t, int lane, Sel<KMAX>& m) {
+  const int K = a.K;
   int s = -1;
   float wt = 0.0f;
   int g = 0;
@@ -89,9 +96,8 @@ __global__ __launch_bounds__(kBlock) void k_combine(CombineArgs a) {
   }
   const bool valid = s >= 0;
   const uint64_t vmask = ballot(valid);
-  const int nv = __popcll(vmask);
-
-  // Rank of each valid selection in summation order: (group, k) ascending.
+  m.nv = __popcll(vmask);
+  // rank of each valid selection in summation order: (group, k) ascending
   int rank;
   if (GROUPED) {
     rank = 0;
@@ -104,94 +110,129 @@ __global__ __launch_bounds__(kBlock) void k_combine(CombineArgs a) {
   } else {
     rank = __popcll(vmask & lanemask_lt());
   }
-
-  // The ordered list, wave-uniform.  Positions past nv repeat the first row
-  // (loads stay in bounds and branch-free) and are never accumulated.
-  int os[KMAX];
-  float ow[KMAX];
-  bool newg[KMAX];
   int gprev = INT_MIN;
 #pragma unroll
   for (int i = 0; i < KMAX; ++i) {
-    const uint64_t m = ballot(valid && rank == (i < nv ? i : 0));
-    const int L = m ? static_cast<int>(__builtin_ctzll(m)) : 0;
-    os[i] = readlane(s, L);
-    ow[i] = __int_as_float(readlane(__float_as_int(wt), L));
+    const uint64_t mk = ballot(valid && rank == (i < m.nv ? i : 0));
+    const int L = mk ? static_cast<int>(__builtin_ctzll(mk)) : 0;
+    m.os[i] = readlane(s, L);
+    m.ow[i] = __int_as_float(readlane(__float_as_int(wt), L));
     const int gi = readlane(g, L);
-    newg[i] = i > 0 && gi != gprev;
+    m.newg[i] = i > 0 && gi != gprev;
     gprev = gi;
   }
+}
 
+// One chunk: U vectors per lane of the token's output row.
+template <int KMAX, int VE, bool GROUPED, int U, bool FULL>
+__device__ __forceinline__ void reduce_chunk(const typename BfVec<VE>::V* __restrict__ yv,
+                                             typename BfVec<VE>::V* __restrict__ outv, int nvec,
+                                             int vb, int lane, const Sel<KMAX>& m) {
+  using B = BfVec<VE>;
+  using V = typename B::V;
+  V in[U][KMAX];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int vi = min(vb + u * kWave + lane, nvec - 1);
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) in[u][i] = nt_load(yv + static_cast<int64_t>(m.os[i]) * nvec + vi);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    float res[VE];
+#pragma unroll
+    for (int e = 0; e < VE; ++e) {
+      float tot = 0.0f, P = 0.0f;
+#pragma unroll
+      for (int i = 0; i < KMAX; ++i) {
+        if (FULL || i < m.nv) {
+          if (GROUPED && m.newg[i]) {
+            tot = __fadd_rn(tot, P);
+            P = 0.0f;
+          }
+          P = __fadd_rn(P, __fmul_rn(m.ow[i], B::get(in[u][i], e)));
+        }
+      }
+      res[e] = GROUPED ? __fadd_rn(tot, P) : P;
+    }
+    const int vi = vb + u * kWave + lane;
+    if (vi < nvec) outv[vi] = B::pack(res);
+  }
+}
+
+template <int KMAX, int VE, bool GROUPED, int U>
+__global__ __launch_bounds__(kBlock) void k_combine(CombineArgs a, int nchunks, int64_t items) {
+  using B = BfVec<VE>;
+  using V = typename B::V;
+  const int lane = threadIdx.x & (kWave - 1);
+  int64_t it, end;
+  wave_range(items, it, end);
+  if (it >= end) return;
+  int64_t t = it / nchunks;
+  int c = static_cast<int>(it - t * nchunks);
   const int nvec = a.H / VE;
   const V* yv = static_cast<const V*>(a.y);
-  V* outv = static_cast<V*>(a.out) + t * nvec;
-  if (nv == 0) {
-    const float zf[VE] = {};
-    const V z = B::pack(zf);
-    for (int vi = lane; vi < nvec; vi += kWave) outv[vi] = z;
-    return;
-  }
-  for (int v0 = 0; v0 < nvec; v0 += kWave * U) {
-    V in[U][KMAX];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int vi = min(v0 + u * kWave + lane, nvec - 1);
-#pragma unroll
-      for (int i = 0; i < KMAX; ++i) in[u][i] = yv[static_cast<int64_t>(os[i]) * nvec + vi];
+  Sel<KMAX> m;
+  load_sel<KMAX, GROUPED>(a, t, lane, m);
+  for (; it < end; ++it, ++c) {
+    if (c == nchunks) {
+      c = 0;
+      ++t;
+      load_sel<KMAX, GROUPED>(a, t, lane, m);
     }
+    V* outv = static_cast<V*>(a.out) + t * nvec;
+    const int vb = c * (kWave * U);
+    if (m.nv == KMAX) {
+      reduce_chunk<KMAX, VE, GROUPED, U, true>(yv, outv, nvec, vb, lane, m);
+    } else if (m.nv > 0) {
+      reduce_chunk<KMAX, VE, GROUPED, U, false>(yv, outv, nvec, vb, lane, m);
+    } else {
+      const float zf[VE] = {};
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float res[VE];
-#pragma unroll
-      for (int e = 0; e < VE; ++e) {
-        float tot = 0.0f, P = 0.0f;
-#pragma unroll
-        for (int i = 0; i < KMAX; ++i) {
-          if (i < nv) {
-            if (GROUPED && newg[i]) {
-              tot = __fadd_rn(tot, P);
-              P = 0.0f;
-            }
-            P = __fadd_rn(P, __fmul_rn(ow[i], B::get(in[u][i], e)));
-          }
-        }
-        res[e] = GROUPED ? __fadd_rn(tot, P) : P;
+      for (int u = 0; u < U; ++u) {
+        const int vi = vb + u * kWave + lane;
+        if (vi < nvec) outv[vi] = B::pack(zf);
       }
-      const int vi = v0 + u * kWave + lane;
-      if (vi < nvec) outv[vi] = B::pack(res);
     }
   }
 }
 
-template <int KMAX, bool GROUPED>
-hipError_t combine_k(const CombineArgs& a, int ve, dim3 grid, hipStream_t s) {
+template <int KMAX, int VE, bool GROUPED>
+hipError_t combine_v(const CombineArgs& a, hipStream_t s) {
   // two row chunks in flight per lane while the K loads stay within registers
   constexpr int U = KMAX <= 8 ? 2 : 1;
-  switch (ve) {
-    case 8: k_combine<KMAX, 8, GROUPED, U><<<grid, kBlock, 0, s>>>(a); break;
-    case 4: k_combine<KMAX, 4, GROUPED, U><<<grid, kBlock, 0, s>>>(a); break;
-    case 2: k_combine<KMAX, 2, GROUPED, U><<<grid, kBlock, 0, s>>>(a); break;
-    default: k_combine<KMAX, 1, GROUPED, U><<<grid, kBlock, 0, s>>>(a); break;
-  }
+  const int nvec = a.H / VE;
+  const int nchunks = (nvec + kWave * U - 1) / (kWave * U);
+  const int64_t items = a.T * nchunks;
+  constexpr auto kern = k_combine<KMAX, VE, GROUPED, U>;
+  kern<<<persistent_blocks<kern>(items), kBlock, 0, s>>>(a, nchunks, items);
   return hipGetLastError();
 }
 
+template <int KMAX, bool GROUPED>
+hipError_t combine_k(const CombineArgs& a, int ve, hipStream_t s) {
+  switch (ve) {
+    case 8: return combine_v<KMAX, 8, GROUPED>(a, s);
+    case 4: return combine_v<KMAX, 4, GROUPED>(a, s);
+    case 2: return combine_v<KMAX, 2, GROUPED>(a, s);
+    default: return combine_v<KMAX, 1, GROUPED>(a, s);
+  }
+}
+
 template <bool GROUPED>
-hipError_t combine_g(const CombineArgs& a, int ve, dim3 grid, hipStream_t s) {
-  if (a.K <= 1) return combine_k<1, GROUPED>(a, ve, grid, s);
-  if (a.K <= 2) return combine_k<2, GROUPED>(a, ve, grid, s);
-  if (a.K <= 4) return combine_k<4, GROUPED>(a, ve, grid, s);
-  if (a.K <= 8) return combine_k<8, GROUPED>(a, ve, grid, s);
-  if (a.K <= 16) return combine_k<16, GROUPED>(a, ve, grid, s);
-  return combine_k<32, GROUPED>(a, ve, grid, s);
+hipError_t combine_g(const CombineArgs& a, int ve, hipStream_t s) {
+  if (a.K <= 1) return combine_k<1, GROUPED>(a, ve, s);
+  if (a.K <= 2) return combine_k<2, GROUPED>(a, ve, s);
+  if (a.K <= 4) return combine_k<4, GROUPED>(a, ve, s);
+  if (a.K <= 8) return combine_k<8, GROUPED>(a, ve, s);
+  if (a.K <= 16) return combine_k<16, GROUPED>(a, ve, s);
+  return combine_k<32, GROUPED>(a, ve, s);
 }
 
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs& a, int vec_elems, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>((a.T + kWavesPerBlock - 1) / kWavesPerBlock));
-  return a.grouped ? combine_g<true>(a, vec_elems, grid, s)
-                   : combine_g<false>(a, vec_elems, grid, s);
+  return a.grouped ? combine_g<true>(a, vec_elems, s) : combine_g<false>(a, vec_elems, s);
 }
 
 }  // namespace ep

@@ -57,6 +57,17 @@ __device__ __forceinline__ uint32_t f32_to_e4m3fn_sat(float v) {
   return code | sign;
 }
 
+// Hardware conversion of two fp32 values to E4M3FN codes (gfx950
+// v_cvt_pk_fp8_f32, round to nearest even, OCP encoding).  Magnitudes are
+// clamped to 448 first (keeping the sign, also of -0.0), which gives the
+// saturating conversion above for every non-NaN input; an exhaustive test
+// over all 2^32 fp32 patterns checks this against f32_to_e4m3fn_sat.
+__device__ __forceinline__ uint32_t e4m3fn_sat_pair(float a, float b) {
+  const float ca = __builtin_copysignf(fminf(fabsf(a), 448.0f), a);
+  const float cb = __builtin_copysignf(fminf(fabsf(b), 448.0f), b);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, 0, false)) & 0xFFFFu;
+}
+
 // ---------------------------------------------------------------- wave utils
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
@@ -76,6 +87,15 @@ __device__ __forceinline__ T nt_load(const T* p) {
 template <typename T>
 __device__ __forceinline__ void nt_store(T v, T* p) {
   __builtin_nontemporal_store(v, p);
+}
+
+// Persistent work split: the grid's waves take contiguous, equal (within
+// one item) ranges of `items`.  Returns [begin, end) for the calling wave.
+__device__ __forceinline__ void wave_range(int64_t items, int64_t& begin, int64_t& end) {
+  const int64_t wave = (static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x) / kWave;
+  const int64_t nw = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
+  begin = wave * items / nw;
+  end = (wave + 1) * items / nw;
 }
 
 // Vectors used for row copies (clang extended vectors: one global

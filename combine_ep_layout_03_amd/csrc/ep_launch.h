@@ -1,0 +1,48 @@
+// Host-side launch shapes for the persistent kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ep_device.h"
+
+namespace ep {
+
+// Compute units of the current device (cached per device id).
+inline int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  if (dev >= 64) {
+    int n = 0;
+    return hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
+  }
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Blocks for a persistent launch of `Kern`: every block the device can keep
+// resident at once, but no more blocks than needed to give each wave one of
+// `items` work items.  Residency is queried once per kernel.
+template <auto Kern>
+inline unsigned persistent_blocks(int64_t items, size_t lds = 0) {
+  static int occ = 0;
+  if (occ == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, Kern, kBlock, lds) != hipSuccess || n < 1)
+      n = 1;
+    occ = n;
+  }
+  const int64_t full = static_cast<int64_t>(device_cus()) * occ;
+  const int64_t need = (items + kWavesPerBlock - 1) / kWavesPerBlock;
+  int64_t b = need < full ? need : full;
+  if (b < 1) b = 1;
+  return static_cast<unsigned>(b);
+}
+
+}  // namespace ep

@@ -121,10 +121,12 @@ def main(argv=None):
     x = W.make_x(w, device=dev)
     y = W.make_y(w, device=dev)  # T*K expert-output rows
     rb = ep.ep_fp8_row_bytes(H)
+    pitch = ep.fp8_row_pitch(H)  # 128-byte aligned receive-row pitch (7424 at H=7168)
 
     L = ep.ep_layout(d_idx, E)
     n_sel = L.num_rows()
-    recv8 = torch.empty(T * K, rb, dtype=torch.uint8, device=dev)
+    recv8 = torch.empty(T * K, pitch, dtype=torch.uint8, device=dev)
+    recv8_packed = torch.empty(T * K, rb, dtype=torch.uint8, device=dev) if args.isolated else None
     out = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
     recv16 = torch.empty(T * K, H, dtype=torch.bfloat16, device=dev) if args.bf16_dispatch else None
     nb = algorithmic_bytes(T, H, K, E, n_sel, rb)
@@ -200,11 +202,14 @@ def main(argv=None):
         iso = {
             "layout": lambda: ep.ep_layout(d_idx, E, out=L),
             "dispatch_fp8": lambda: ep.ep_dispatch(x, L, fp8=True, out=recv8),
+            "dispatch_fp8_packed_pitch": lambda: ep.ep_dispatch(x, L, fp8=True, out=recv8_packed),
             "combine": lambda: ep.ep_combine(y, L, d_wt, out=out),
         }
         if recv16 is not None:
             iso["dispatch_bf16"] = lambda: ep.ep_dispatch(x, L, fp8=False, out=recv16)
         for name, fn in iso.items():
+            if name not in ops:
+                ops[name] = {"bytes": nb["dispatch_fp8"]}
             fn()
             a0 = torch.cuda.Event(enable_timing=True)
             a1 = torch.cuda.Event(enable_timing=True)
@@ -215,7 +220,7 @@ def main(argv=None):
             torch.cuda.synchronize()
             us = a0.elapsed_time(a1) * 1e3 / args.steps
             ops[name]["isolated_us"] = round(us, 2)
-            ops[name]["isolated_GBps"] = round(nb[name] / (us * 1e-6) / 1e9, 1)
+            ops[name]["isolated_GBps"] = round(ops[name]["bytes"] / (us * 1e-6) / 1e9, 1)
     step_bytes = nb["layout"] + nb["dispatch_fp8"] + nb["combine"]
     step_ms = statistics.median(t_step)
     value = step_bytes / (step_ms * 1e-3) / 1e9
@@ -245,7 +250,7 @@ def main(argv=None):
         "data": "synthetic",
         "config": {
             "workload": f"{w.name}: T={T} tokens, H={H}, top-{K} of E={E} experts, uniform routing; "
-            "fp8 packed dispatch + bf16 combine",
+            f"fp8 packed dispatch ({rb}-byte rows at a {pitch}-byte receive pitch) + bf16 combine",
             "global_batch": T,
             "seq_len": 1,
             "parallelism": "single-GPU",

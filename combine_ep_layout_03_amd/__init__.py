@@ -34,6 +34,7 @@ from ._lib import (  # noqa: F401
 __all__ = [
     "Layout",
     "ep_fp8_row_bytes",
+    "fp8_row_pitch",
     "ep_layout_workspace_bytes",
     "ep_layout",
     "ep_dispatch",
@@ -72,6 +73,13 @@ def _problem(T: int, H: int, K: int, E: int, G: int) -> _lib.Problem:
 def ep_fp8_row_bytes(hidden: int) -> int:
     """Bytes of one packed fp8 row (H payload bytes, H/128 fp32 scales, 16-byte pad)."""
     return int(_lib.lib().ep_fp8_row_bytes(hidden))
+
+
+def fp8_row_pitch(hidden: int, align: int = 128) -> int:
+    """The packed fp8 row size rounded up to `align` bytes: a receive-row
+    pitch that keeps every row on an aligned boundary (7424 for hidden 7168)."""
+    rb = ep_fp8_row_bytes(hidden)
+    return -1 if rb < 0 else (rb + align - 1) // align * align
 
 
 def ep_layout_workspace_bytes(num_tokens: int, topk: int, num_experts: int, num_groups: int = 0) -> int:
@@ -208,12 +216,17 @@ def ep_dispatch(
     rows: int = EP_ROWS_EXPERT,
     capacity: int | None = None,
     out: torch.Tensor | None = None,
+    row_stride: int | None = None,
 ) -> torch.Tensor:
     """Scatter token rows x (bf16 [T, H]) to their receive rows.
 
     Returns ``out``: bf16 [capacity, H], or uint8 [capacity, ep_fp8_row_bytes(H)]
-    with ``fp8``.  The default capacity is the worst case (T*K expert rows,
-    min(T*G, T*K) group rows), so no host synchronisation is needed."""
+    with ``fp8``.  The receive-row pitch is the row size of ``out`` (one row
+    of the 2-D tensor per receive row); when ``out`` is allocated here it is
+    ``row_stride`` bytes (default: the row size, rows packed back to back).
+    Only the first row-size bytes of each row are written.  The default
+    capacity is the worst case (T*K expert rows, min(T*G, T*K) group rows),
+    so no host synchronisation is needed."""
     if x.dim() != 2 or x.shape[0] != layout.num_tokens:
         raise ValueError("x must be [T, H] with the layout's T")
     _dev(x, "x", torch.bfloat16)
@@ -221,27 +234,38 @@ def ep_dispatch(
     if capacity is None:
         capacity = T * layout.topk if rows == EP_ROWS_EXPERT else layout.max_group_rows()
     fmt = EP_FORMAT_FP8_PACKED if fp8 else EP_FORMAT_BF16
-    if out is None:
-        if fp8:
-            rb = ep_fp8_row_bytes(H)
-            if rb < 0:
-                raise _lib.EPError("ep_dispatch", _lib.EP_ENOTSUP, "fp8 rows need hidden % 128 == 0")
-            out = torch.empty(max(capacity, 1), rb, dtype=torch.uint8, device=x.device)
-        else:
-            out = torch.empty(max(capacity, 1), H, dtype=torch.bfloat16, device=x.device)
+    if fp8:
+        rb = ep_fp8_row_bytes(H)
+        if rb < 0:
+            raise _lib.EPError("ep_dispatch", _lib.EP_ENOTSUP, "fp8 rows need hidden % 128 == 0")
+        dtype, esize = torch.uint8, 1
     else:
-        if fp8:
-            _dev(out, "out", torch.uint8)
-            if out.dim() != 2 or out.shape[1] != ep_fp8_row_bytes(H) or out.shape[0] < capacity:
-                raise ValueError("out must be uint8 [>= capacity, ep_fp8_row_bytes(H)]")
-        else:
-            _dev(out, "out", torch.bfloat16)
-            if out.dim() != 2 or out.shape[1] != H or out.shape[0] < capacity:
-                raise ValueError("out must be bf16 [>= capacity, H]")
+        rb = 2 * H
+        dtype, esize = torch.bfloat16, 2
+    if out is None:
+        pitch = rb if row_stride is None else int(row_stride)
+        if pitch < rb or pitch % esize:
+            raise ValueError(f"row_stride must be a multiple of {esize} and >= {rb}")
+        out = torch.empty(max(capacity, 1), pitch // esize, dtype=dtype, device=x.device)
+    else:
+        _dev(out, "out", dtype)
+        if out.dim() != 2 or out.shape[1] * esize < rb or out.shape[0] < capacity:
+            raise ValueError(f"out must be {dtype} [>= capacity, >= {rb // esize}]")
+        if row_stride is not None and row_stride != out.shape[1] * esize:
+            raise ValueError("row_stride disagrees with out's row size")
+    pitch = out.shape[1] * esize
     p = _problem(T, H, layout.topk, layout.num_experts, layout.num_groups)
     s = layout.struct()
     rc = _lib.lib().ep_dispatch(
-        ctypes.byref(p), ctypes.byref(s), _ptr(x), _ptr(out), int(capacity), int(rows), fmt, _stream(x.device)
+        ctypes.byref(p),
+        ctypes.byref(s),
+        _ptr(x),
+        _ptr(out),
+        int(capacity),
+        int(pitch),
+        int(rows),
+        fmt,
+        _stream(x.device),
     )
     _lib.check("ep_dispatch", rc)
     return out

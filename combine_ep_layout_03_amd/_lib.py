@@ -100,7 +100,7 @@ def lib(path: str | None = None) -> ctypes.CDLL:
     L.ep_layout_workspace_bytes.restype = ctypes.c_size_t
     L.ep_layout.argtypes = [P, vp, vp, LS, vp, ctypes.c_size_t, vp]
     L.ep_layout.restype = ctypes.c_int
-    L.ep_dispatch.argtypes = [P, LS, vp, vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, vp]
+    L.ep_dispatch.argtypes = [P, LS, vp, vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, vp]
     L.ep_dispatch.restype = ctypes.c_int
     L.ep_combine.argtypes = [P, LS, vp, vp, vp, ctypes.c_int64, vp, ctypes.c_int32, vp]
     L.ep_combine.restype = ctypes.c_int

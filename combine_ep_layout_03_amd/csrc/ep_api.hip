@@ -93,22 +93,25 @@ int ep_layout(const ep_problem_t* p, const int64_t* topk_idx, const float* topk_
 }
 
 int ep_dispatch(const ep_problem_t* p, const ep_layout_t* L, const void* x, void* recv,
-                int64_t capacity_rows, int32_t rows, int32_t format, hipStream_t stream) {
+                int64_t capacity_rows, int64_t recv_row_stride, int32_t rows, int32_t format,
+                hipStream_t stream) {
   int rc = check_problem(p);
   if (rc != EP_OK) return rc;
-  if (!L || !L->status || capacity_rows < 0) return EP_EINVAL;
+  if (!L || !L->status || capacity_rows < 0 || recv_row_stride < 0) return EP_EINVAL;
   if (rows != EP_ROWS_EXPERT && rows != EP_ROWS_GROUP) return EP_EINVAL;
   if (format != EP_FORMAT_BF16 && format != EP_FORMAT_FP8_PACKED) return EP_EINVAL;
   if (rows == EP_ROWS_GROUP && p->num_groups < 1) return EP_EINVAL;
-  int64_t fp8_rb = 0;
+  int64_t row_bytes = static_cast<int64_t>(p->hidden) * 2;
   if (format == EP_FORMAT_FP8_PACKED) {
-    fp8_rb = ep_fp8_row_bytes(p->hidden);
-    if (fp8_rb < 0) return EP_ENOTSUP;
+    row_bytes = ep_fp8_row_bytes(p->hidden);
+    if (row_bytes < 0 || p->hidden > 32768) return EP_ENOTSUP;
   }
+  const int64_t stride = recv_row_stride == 0 ? row_bytes : recv_row_stride;
+  if (stride < row_bytes) return EP_EINVAL;
   if (p->num_tokens == 0) return EP_OK;
   const int32_t* dest = rows == EP_ROWS_EXPERT ? L->slot : L->grow;
   if (!dest || !x || (!recv && capacity_rows > 0)) return EP_EINVAL;
-  if (!aligned(x, 2) || !aligned(recv, 2)) return EP_EINVAL;
+  if (!aligned(x, 2) || !aligned(recv, 2) || stride % 2 != 0) return EP_EINVAL;
 
   ep::ScatterArgs a;
   a.x = x;
@@ -119,14 +122,16 @@ int ep_dispatch(const ep_problem_t* p, const ep_layout_t* L, const void* x, void
   a.K = p->topk;
   a.H = p->hidden;
   a.capacity = capacity_rows;
+  a.stride = stride;
   a.dedup = rows == EP_ROWS_GROUP;
   hipError_t err;
   if (format == EP_FORMAT_FP8_PACKED) {
-    if (!aligned(x, 16) || !aligned(recv, 16)) return EP_EINVAL;
-    err = ep::launch_scatter_fp8(a, fp8_rb, stream);
+    if (!aligned(x, 16) || !aligned(recv, 16) || stride % 16 != 0) return EP_EINVAL;
+    err = ep::launch_scatter_fp8(a, row_bytes, stream);
   } else {
-    err = ep::launch_scatter_bf16(a, vec_bytes_for(static_cast<int64_t>(p->hidden) * 2, x, recv),
-                                  stream);
+    int vb = vec_bytes_for(row_bytes, x, recv);
+    while (stride % vb != 0) vb >>= 1;
+    err = ep::launch_scatter_bf16(a, vb, stream);
   }
   return err == hipSuccess ? EP_OK : EP_EHIP;
 }
@@ -169,7 +174,8 @@ const char* ep_strerror(int code) {
   switch (code) {
     case EP_OK: return "ok";
     case EP_EINVAL: return "invalid argument (null pointer, bad size or misaligned base)";
-    case EP_ENOTSUP: return "unsupported (fp8 needs hidden % 128 == 0; K <= 32; E + G <= 1024)";
+    case EP_ENOTSUP:
+      return "unsupported (fp8 needs hidden % 128 == 0 and hidden <= 32768; K <= 32; E + G <= 1024)";
     case EP_EHIP: return "HIP launch failed";
     case EP_EWORKSPACE: return "workspace smaller than ep_layout_workspace_bytes()";
     default: return "unknown error code";

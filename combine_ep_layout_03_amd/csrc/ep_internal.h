@@ -47,12 +47,13 @@ struct ScatterArgs {
   int K;
   int H;
   int64_t capacity;
+  int64_t stride;  // bytes from one receive row to the next
   bool dedup;  // several k may name one row (grouped rows)
 };
-// bf16 rows; `vec_bytes` in {16, 8, 4, 2} divides the row size and both
-// base alignments.
+// bf16 rows; `vec_bytes` in {16, 8, 4, 2} divides the row size, the stride
+// and both base alignments.
 hipError_t launch_scatter_bf16(const ScatterArgs& a, int vec_bytes, hipStream_t s);
-// packed fp8 rows; H % 128 == 0, 16-byte aligned bases.
+// packed fp8 rows; H % 128 == 0, H <= 32768, 16-byte aligned bases and stride.
 hipError_t launch_scatter_fp8(const ScatterArgs& a, int64_t row_bytes, hipStream_t s);
 
 struct CombineArgs {

@@ -150,19 +150,29 @@ int ep_layout(const ep_problem_t* p, const int64_t* topk_idx, const float* topk_
  * the layout assigned it.
  *   rows == EP_ROWS_EXPERT: recv row slot[t,k] for each valid (t,k);
  *   rows == EP_ROWS_GROUP:  recv row grow[t,k] once per distinct row.
- *   format == EP_FORMAT_BF16:       recv is bf16 [capacity_rows * H];
- *   format == EP_FORMAT_FP8_PACKED: recv is uint8 [capacity_rows * ep_fp8_row_bytes(H)],
- *     each row quantised per 128-element group j as s_j = amax_j / 448 and
- *     q = E4M3FN(x / s_j) (both fp32 IEEE divisions, round to nearest even,
- *     saturating at 448; s_j == 0 gives q = 0), requires H % 128 == 0.
+ *   format == EP_FORMAT_BF16: a receive row is the token's H bf16 values
+ *     (2*H bytes);
+ *   format == EP_FORMAT_FP8_PACKED: a receive row is the packed fp8 row of
+ *     ep_fp8_row_bytes(H) bytes, quantised per 128-element group j as
+ *     s_j = amax_j / 448 and q = E4M3FN(x / s_j) (both fp32 IEEE divisions,
+ *     round to nearest even, saturating at 448; s_j == 0 gives q = 0);
+ *     requires H % 128 == 0 and H <= 32768.
+ * Receive row r starts at byte r * recv_row_stride of recv; recv_row_stride
+ * == 0 means the row size itself (rows packed back to back).  A larger
+ * stride pads each row to an aligned pitch (for the fp8 row at hidden 7168,
+ * 7424 bytes puts every row on a 128-byte boundary, which MI355X writes
+ * markedly faster than the packed 7392); the bytes between a row's end and
+ * the next row are never written.  recv must hold capacity_rows rows.
  * Each source row is read once and written once per destination row.  If
  * the rows needed (status word EP_STATUS_ROWS_EXPERT or _GROUP) exceed
  * capacity_rows the call writes nothing: an overflow is known before any
  * payload moves.  Rows at or beyond the rows needed are never touched.
- * Base pointers of x and recv must be 16-byte aligned for the fp8 format;
- * for bf16 any 2-byte alignment works (wider alignment is faster). */
+ * Base pointers of x and recv, and the stride, must be 16-byte aligned for
+ * the fp8 format; for bf16 any 2-byte alignment works (wider alignment is
+ * faster). */
 int ep_dispatch(const ep_problem_t* p, const ep_layout_t* L, const void* x, void* recv,
-                int64_t capacity_rows, int32_t rows, int32_t format, hipStream_t stream);
+                int64_t capacity_rows, int64_t recv_row_stride, int32_t rows, int32_t format,
+                hipStream_t stream);
 
 /* Combine: out[t] (bf16 [T*H]) = bf16_rne of the fp32 sum over the token's
  * valid selections of topk_weights[t,k] * y[slot[t,k]], with y bf16

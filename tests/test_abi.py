@@ -60,24 +60,30 @@ def test_invalid_arguments_return_codes_before_any_launch():
     assert L.ep_layout(ctypes.byref(p), None, None, ctypes.byref(lay), None, 0, None) == _lib.EP_EINVAL
     # bad shapes
     bad = _lib.Problem(16, 256, 0, 256, 0)
-    assert L.ep_dispatch(ctypes.byref(bad), ctypes.byref(lay), None, None, 0, 0, 0, None) == _lib.EP_EINVAL
+    assert L.ep_dispatch(ctypes.byref(bad), ctypes.byref(lay), None, None, 0, 0, 0, 0, None) == _lib.EP_EINVAL
     bad = _lib.Problem(16, 256, 8, 256, 3)
     assert L.ep_combine(ctypes.byref(bad), ctypes.byref(lay), None, None, None, 0, None, 0, None) == _lib.EP_EINVAL
     # fp8 with hidden % 128 != 0 is unsupported (checked before pointers)
     p2 = _lib.Problem(16, 100, 8, 256, 0)
     lay.status = 8  # any non-null value; never dereferenced on this path
     assert (
-        L.ep_dispatch(ctypes.byref(p2), ctypes.byref(lay), None, None, 0, _lib.EP_ROWS_EXPERT, _lib.EP_FORMAT_FP8_PACKED, None)
+        L.ep_dispatch(ctypes.byref(p2), ctypes.byref(lay), None, None, 0, 0, _lib.EP_ROWS_EXPERT, _lib.EP_FORMAT_FP8_PACKED, None)
         == _lib.EP_ENOTSUP
     )
     # grouped rows without groups
     assert (
-        L.ep_dispatch(ctypes.byref(p), ctypes.byref(lay), None, None, 0, _lib.EP_ROWS_GROUP, _lib.EP_FORMAT_BF16, None)
+        L.ep_dispatch(ctypes.byref(p), ctypes.byref(lay), None, None, 0, 0, _lib.EP_ROWS_GROUP, _lib.EP_FORMAT_BF16, None)
         == _lib.EP_EINVAL
     )
     # T = 0 dispatch / combine are valid no-ops that launch nothing
     p0 = _lib.Problem(0, 256, 8, 256, 0)
-    assert L.ep_dispatch(ctypes.byref(p0), ctypes.byref(lay), None, None, 0, 0, 0, None) == _lib.EP_OK
+    assert L.ep_dispatch(ctypes.byref(p0), ctypes.byref(lay), None, None, 0, 0, 0, 0, None) == _lib.EP_OK
+    # a stride below the row size is rejected
+    p3 = _lib.Problem(16, 256, 8, 256, 0)
+    assert L.ep_dispatch(ctypes.byref(p3), ctypes.byref(lay), None, None, 0, 256, 0, 0, None) == _lib.EP_EINVAL
+    # fp8 beyond the hidden limit
+    p4 = _lib.Problem(16, 32768 + 128, 8, 256, 0)
+    assert L.ep_dispatch(ctypes.byref(p4), ctypes.byref(lay), None, None, 0, 0, 0, 1, None) == _lib.EP_ENOTSUP
     assert L.ep_combine(ctypes.byref(p0), ctypes.byref(lay), None, None, None, 0, None, 0, None) == _lib.EP_OK
 
 

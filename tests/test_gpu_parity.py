@@ -271,6 +271,34 @@ def test_dispatch_poison_and_capacity():
     assert bool((out3 == 0xAB).all())
 
 
+@pytest.mark.parametrize("fp8,H,pitch", [(True, 7168, 7424), (True, 128, 256), (True, 384, 416), (False, 136, 512), (False, 9, 20)])
+def test_dispatch_row_pitch(fp8, H, pitch):
+    """Rows at a padded pitch: row bytes equal the oracle's, gap bytes untouched."""
+    say("dispatch pitch", fp8, H, pitch)
+    w = W.Workload("pitch", T=700 if H > 1000 else 1500, H=H, K=8, E=64, mask_p=0.1, seed=H + pitch)
+    idx, _ = W.make_routing(w)
+    x = W.make_x(w)
+    R = O.layout(idx.numpy(), w.E)
+    L = ep().ep_layout(idx.to(DEV), w.E)
+    n = R["n_sel"]
+    cap = w.T * w.K
+    if fp8:
+        rb = O.fp8_row_bytes(H)
+        out = torch.full((cap, pitch), 0xA5, dtype=torch.uint8, device=DEV)
+        ep().ep_dispatch(x.to(DEV), L, fp8=True, out=out)
+        got = out.cpu().numpy()
+        want = O.dispatch_fp8(u16(x), R["slot"], n)
+        assert np.array_equal(got[:n, :rb], want)
+        assert (got[:n, rb:] == 0xA5).all() and (got[n:] == 0xA5).all()
+    else:
+        out = torch.full((cap, pitch // 2), -23131, dtype=torch.int16, device=DEV)  # 0xA5A5
+        ep().ep_dispatch(x.to(DEV), L, out=out.view(torch.bfloat16))
+        got = out.cpu().numpy().view(np.uint16)
+        want = O.dispatch_bf16(u16(x), R["slot"], n)
+        assert np.array_equal(got[:n, :H], want)
+        assert (got[:n, H:] == 0xA5A5).all() and (got[n:] == 0xA5A5).all()
+
+
 def test_dispatch_grouped_rows_small():
     w = W.by_name("grouped").replace(T=3000, H=264, mask_p=0.1)
     idx, wt = W.make_routing(w)

@@ -36,6 +36,27 @@ def algorithmic_bytes(T, H, K, E, n_sel, fp8_row_bytes):
     return {"layout": layout, "dispatch_fp8": disp_fp8, "dispatch_bf16": disp_bf16, "combine": combine}
 
 
+def counted_traffic(op, workload):
+    """HBM bytes per launch of `op` from the committed FETCH_SIZE/WRITE_SIZE
+    passes (profiles/traffic_<op>_<workload>.json), or None when there is no
+    such record or the kernel sources changed since the counters were taken
+    (the record keeps a hash of the sources it was measured on)."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"traffic_{op}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    h = hashlib.sha256()
+    for f in rec.get("sources", []):
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest()[:16] != rec.get("source_sha256_16"):
+        return None
+    return rec.get("bytes_per_launch")
+
+
 def cpu_baseline(w, idx, wt, x_host, y_host, sample_tokens):
     """The CPU oracle, as it stands, timed on a bounded sample of the workload:
     the full layout, then fp8 dispatch and combine of the first
@@ -93,6 +114,14 @@ def main(argv=None):
         "--isolated",
         action="store_true",
         help="also time each op alone, back to back, outside the step (diagnostic)",
+    )
+    ap.add_argument(
+        "--calibrate-copy",
+        type=int,
+        default=0,
+        metavar="MIB",
+        help="after the run, copy a MIB-mebibyte buffer 5 times with torch (a plain copy "
+        "kernel of known size, the reference for HBM byte counters)",
     )
     args = ap.parse_args(argv)
     if args.gpus != 1:
@@ -229,11 +258,7 @@ def main(argv=None):
     dom = max(("dispatch_fp8", "combine"), key=lambda k: ops[k]["us_median"])
     avg_us = statistics.mean(t_disp if dom == "dispatch_fp8" else t_comb) * 1e3
     achieved = nb[dom] / (avg_us * 1e-6) / 1e9
-    traffic = None
-    tfile = os.path.join(ROOT, "profiles", f"traffic_{dom}_{w.name}.json")
-    if os.path.exists(tfile):
-        with open(tfile) as fh:
-            traffic = json.load(fh).get("bytes_per_launch")
+    traffic = counted_traffic(dom, w.name)
 
     res = {
         "metric": METRIC,
@@ -274,6 +299,15 @@ def main(argv=None):
         S = args.cpu_sample_tokens
         y_host = y[: int(n_sel)].cpu().view(torch.int16).numpy().view(np.uint16)
         res["cpu_baseline"] = cpu_baseline(w, idx.numpy(), wt.numpy(), x_host, y_host, S)
+    if args.calibrate_copy:
+        nbytes = args.calibrate_copy << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        res["calibrate_copy_bytes"] = nbytes
     print(json.dumps(res), flush=True)
     return 0
 

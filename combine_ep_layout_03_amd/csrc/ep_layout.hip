@@ -105,7 +105,11 @@ __global__ __launch_bounds__(kBlock) void k_layout_count(const int64_t* __restri
 }
 
 // In-place exclusive scan of each column over the nblocks rows; the column
-// totals go to row nblocks.  Block = 64 columns x 16 row slices.
+// totals go to row nblocks.  Block = 64 columns x 16 row slices; a slice
+// holds at most kScanRows rows (nblocks <= 16 * kScanRows), loaded at once
+// and kept in registers for the write-back.
+constexpr int kScanRows = 16;
+
 __global__ __launch_bounds__(1024) void k_layout_colscan(int* __restrict__ partials, int nblocks,
                                                          int ncols) {
   __shared__ int s[16][kWave + 1];
@@ -113,30 +117,35 @@ __global__ __launch_bounds__(1024) void k_layout_colscan(int* __restrict__ parti
   const int rl = threadIdx.x / kWave;
   const int c = blockIdx.x * kWave + cl;
   const int chunk = (nblocks + 15) / 16;
-  const int b0 = min(nblocks, rl * chunk);
-  const int b1 = min(nblocks, b0 + chunk);
+  const int b0 = rl * chunk;
+  int v[kScanRows];
   int sum = 0;
-  if (c < ncols)
-    for (int b = b0; b < b1; ++b) sum += partials[static_cast<size_t>(b) * ncols + c];
+#pragma unroll
+  for (int j = 0; j < kScanRows; ++j) {
+    const int b = b0 + j;
+    v[j] = (j < chunk && b < nblocks && c < ncols) ? partials[static_cast<size_t>(b) * ncols + c] : 0;
+    sum += v[j];
+  }
   s[rl][cl] = sum;
   __syncthreads();
   if (rl == 0) {
     int run = 0;
+#pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const int v = s[j][cl];
+      const int x = s[j][cl];
       s[j][cl] = run;
-      run += v;
+      run += x;
     }
     if (c < ncols) partials[static_cast<size_t>(nblocks) * ncols + c] = run;
   }
   __syncthreads();
-  if (c < ncols) {
-    int run = s[rl][cl];
-    for (int b = b0; b < b1; ++b) {
-      const size_t o = static_cast<size_t>(b) * ncols + c;
-      const int v = partials[o];
-      partials[o] = run;
-      run += v;
+  int run = s[rl][cl];
+#pragma unroll
+  for (int j = 0; j < kScanRows; ++j) {
+    const int b = b0 + j;
+    if (j < chunk && b < nblocks && c < ncols) {
+      partials[static_cast<size_t>(b) * ncols + c] = run;
+      run += v[j];
     }
   }
 }
@@ -156,6 +165,9 @@ __global__ __launch_bounds__(kBlock) void k_layout_place(LayoutArgs a, int ncols
   const int wave = tid / kWave;
   const int lane = tid & (kWave - 1);
   const int* tot = a.partials + static_cast<size_t>(nblocks) * ncols;
+  const uint32_t base = blockIdx.x * static_cast<uint32_t>(rounds) * kBlock;
+  // the first round's id, loaded early so its latency overlaps the scans
+  int64_t v_next = (base + tid < a.n) ? a.idx[base + tid] : -1;
 
   // Segment bases: exclusive prefix sums of the totals, over the experts and
   // (separately) over the groups.
@@ -200,11 +212,14 @@ __global__ __launch_bounds__(kBlock) void k_layout_place(LayoutArgs a, int ncols
   uint64_t* wbm = bm + wave * nkeys;
   const uint64_t bit = 1ull << lane;
   const uint64_t lt = lanemask_lt();
-  const uint32_t base = blockIdx.x * static_cast<uint32_t>(rounds) * kBlock;
   for (int r = 0; r < rounds; ++r) {
     const uint32_t i = base + static_cast<uint32_t>(r) * kBlock + tid;
     const bool in = i < a.n;
-    const int64_t v = in ? a.idx[i] : -1;
+    const int64_t v = v_next;
+    if (r + 1 < rounds) {
+      const uint32_t i2 = i + kBlock;
+      v_next = i2 < a.n ? a.idx[i2] : -1;
+    }
     const bool valid = in && v >= 0 && v < E;
     const int e = valid ? static_cast<int>(v) : -1;
     int kg = -1, g = 0;
@@ -264,7 +279,8 @@ __global__ __launch_bounds__(kBlock) void k_layout_place(LayoutArgs a, int ncols
 
 LayoutGeom layout_geom(int64_t n_entries, int E, int G) {
   LayoutGeom g;
-  // about 256 blocks at most, each thread taking `rounds` entries
+  // at most 256 blocks (the column scan's limit, 16 * kScanRows), each
+  // thread taking `rounds` entries
   const int64_t per_round = static_cast<int64_t>(kBlock) * 256;
   int64_t rounds = (n_entries + per_round - 1) / per_round;
   if (rounds < 1) rounds = 1;

@@ -150,16 +150,23 @@ def fp8_row_bytes(hidden: int) -> int:
 # --------------------------------------------------------------------------
 # layout: count, exclusive scan, slot
 # --------------------------------------------------------------------------
-def layout(topk_idx, num_experts: int, num_groups: int = 0, topk_weights=None) -> dict:
+def layout(
+    topk_idx, num_experts: int, num_groups: int = 0, topk_weights=None, expert_alignment: int = 0
+) -> dict:
     """Placement of every selection, as the three dispatch phases define it.
 
     Expert-major layout (always computed):
       valid(t,k)  <=> 0 <= idx[t,k] < E; -1 is "no selection"; any other id is
                       counted in ``n_invalid`` and treated as -1;
       counts[e]   = #valid (t,k) with idx[t,k] = e;
-      offsets     = exclusive prefix sum of counts (offsets[E] = n_sel);
+      offsets     = exclusive prefix sum of the segment sizes, where a
+                    segment is counts[e] rounded up to a multiple of the
+                    expert alignment A (A <= 1: no rounding; the commit
+                    adding do_expand rounds each segment up and marks the
+                    gap unoccupied); offsets[E] = n_rows_expert;
       slot[t,k]   = offsets[e] + #valid (t',k') before (t,k) in (t,k) order
-                    with the same expert, or -1.
+                    with the same expert, or -1;
+      expert_row_src[r] = the token of expert row r, or -1 for a padding row.
     The pages leave the order of rows inside a segment to whichever lane
     claims a slot first; this oracle fixes ascending (t,k).
 
@@ -194,9 +201,11 @@ def layout(topk_idx, num_experts: int, num_groups: int = 0, topk_weights=None) -
             if vl[t][k]:
                 counts[idl[t][k]] += 1
     # phase 2: exclusive prefix sum -> segment bases
+    A = max(1, int(expert_alignment))
     offsets = [0] * (E + 1)
     for e in range(E):
-        offsets[e + 1] = offsets[e] + counts[e]
+        seg = (counts[e] + A - 1) // A * A
+        offsets[e + 1] = offsets[e] + seg
     # phase 3: base + locally claimed slot, claims taken in (t,k) order
     claimed = [0] * E
     slot = [[-1] * K for _ in range(T)]
@@ -206,12 +215,19 @@ def layout(topk_idx, num_experts: int, num_groups: int = 0, topk_weights=None) -
                 e = idl[t][k]
                 slot[t][k] = offsets[e] + claimed[e]
                 claimed[e] += 1
+    expert_row_src = [-1] * offsets[E]
+    for t in range(T):
+        for k in range(K):
+            if slot[t][k] >= 0:
+                expert_row_src[slot[t][k]] = t
     out = {
         "counts": np.array(counts, dtype=np.int64),
         "offsets": np.array(offsets, dtype=np.int64),
         "slot": np.array(slot, dtype=np.int64).reshape(T, K),
+        "expert_row_src": np.array(expert_row_src, dtype=np.int64),
         "n_invalid": n_invalid,
-        "n_sel": offsets[E],
+        "n_sel": sum(counts),
+        "n_rows_expert": offsets[E],
     }
     if G == 0:
         return out
@@ -272,18 +288,15 @@ def dispatch_bf16(x_u16, dest, n_rows: int) -> np.ndarray:
 
     ``dest`` is ``slot`` for the expert-major layout or ``grow`` for the
     grouped one (several k of a token then name the same row, which receives
-    the same bytes)."""
+    the same bytes).  Rows no selection names are alignment padding and are
+    zero (the zero_padding form)."""
     x = np.asarray(x_u16, dtype=np.uint16)
     dest = np.asarray(dest, dtype=np.int64)
     T, K = dest.shape
     recv = np.zeros((n_rows, x.shape[1]), dtype=np.uint16)
-    written = np.zeros(n_rows, dtype=bool)
     for k in range(K):
         sel = dest[:, k] >= 0
         recv[dest[sel, k]] = x[sel]
-        written[dest[sel, k]] = True
-    if not written.all():
-        raise AssertionError("dispatch_bf16: a receive row was never written")
     return recv
 
 
@@ -315,7 +328,8 @@ def quantize_row_fp8(x_row_u16) -> np.ndarray:
 
 
 def dispatch_fp8(x_u16, dest, n_rows: int) -> np.ndarray:
-    """recv[dest[t,k]] = packed fp8 row of token t (see ``quantize_row_fp8``)."""
+    """recv[dest[t,k]] = packed fp8 row of token t (see ``quantize_row_fp8``);
+    rows no selection names (alignment padding) are all zero bytes."""
     x = np.asarray(x_u16, dtype=np.uint16)
     dest = np.asarray(dest, dtype=np.int64)
     T, K = dest.shape
@@ -336,16 +350,30 @@ def dispatch_fp8(x_u16, dest, n_rows: int) -> np.ndarray:
 # --------------------------------------------------------------------------
 # combine
 # --------------------------------------------------------------------------
-def combine(y_u16, slot, topk_weights) -> np.ndarray:
+def _bias_seed(bias0, bias1, shape) -> np.ndarray:
+    """The combine accumulator's starting value: +0 without a bias,
+    f32(bias) with one, fl32(f32(bias0) + f32(bias1)) with two.  The bias
+    seeds the reduction instead of being added after it (commit adding
+    receive stats and combine bias)."""
+    given = [b for b in (bias0, bias1) if b is not None]
+    if not given:
+        return np.zeros(shape, dtype=np.float32)
+    acc = bf16_to_f32(np.asarray(given[0], dtype=np.uint16)).reshape(shape).astype(np.float32)
+    if len(given) == 2:
+        acc = (acc + bf16_to_f32(np.asarray(given[1], dtype=np.uint16)).reshape(shape)).astype(np.float32)
+    return acc
+
+
+def combine(y_u16, slot, topk_weights, bias0=None, bias1=None) -> np.ndarray:
     """out[t] = bf16_rne(sum over k = 0..K-1 with slot[t,k] >= 0 of
-    w[t,k] * y[slot[t,k]]), accumulated in fp32 from +0 with the product and
-    the sum rounded separately, in ascending k.  A token with no selection
-    gives +0."""
+    w[t,k] * y[slot[t,k]]), accumulated in fp32 with the product and the sum
+    rounded separately, in ascending k, starting from +0 or from the bias
+    (``_bias_seed``).  A token with no selection gives +0, or its bias."""
     y = np.asarray(y_u16, dtype=np.uint16)
     slot = np.asarray(slot, dtype=np.int64)
     w = np.asarray(topk_weights, dtype=np.float32)
     T, K = slot.shape
-    acc = np.zeros((T, y.shape[1]), dtype=np.float32)
+    acc = _bias_seed(bias0, bias1, (T, y.shape[1]))
     for k in range(K):
         sel = slot[:, k] >= 0
         rows = bf16_to_f32(y[slot[sel, k]])
@@ -354,11 +382,13 @@ def combine(y_u16, slot, topk_weights) -> np.ndarray:
     return bf16_rne(acc)
 
 
-def combine_grouped(y_u16, topk_idx, slot, topk_weights, num_experts: int, num_groups: int):
+def combine_grouped(
+    y_u16, topk_idx, slot, topk_weights, num_experts: int, num_groups: int, bias0=None, bias1=None
+):
     """out[t] = bf16_rne(sum over g ascending of P_g) where
     P_g = sum over k ascending with (t,k) valid and in group g of
-    w[t,k] * y[slot[t,k]]; every product and sum is one fp32 rounding and
-    both sums start from +0.  A token's rows inside one group are summed
+    w[t,k] * y[slot[t,k]]; every product and sum is one fp32 rounding; each
+    P_g starts from +0 and the cross-group total from +0 or the bias.  A token's rows inside one group are summed
     before the cross-group sum, as the expanded combine sums a token's
     local-expert rows before sending one row per destination."""
     y = np.asarray(y_u16, dtype=np.uint16)
@@ -367,7 +397,7 @@ def combine_grouped(y_u16, topk_idx, slot, topk_weights, num_experts: int, num_g
     w = np.asarray(topk_weights, dtype=np.float32)
     T, K = slot.shape
     epg = num_experts // num_groups
-    tot = np.zeros((T, y.shape[1]), dtype=np.float32)
+    tot = _bias_seed(bias0, bias1, (T, y.shape[1]))
     for g in range(num_groups):
         P = np.zeros_like(tot)
         for k in range(K):

@@ -1,0 +1,111 @@
+"""Pins for the oracle's expert alignment / padding rows and combine bias.
+
+Alignment is checked by an exhaustive brute force over small routings
+(segment bases from a sort of (e, t, k) tuples plus a closed-form rounding),
+by its reduction to the unaligned layout, and by invariants.  The bias is
+checked by the cases the pages state (a fully masked token returns its
+bias), a zero bias reducing to no bias, and a float64 bound.
+"""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import ep_oracle as O
+import workloads as W
+
+
+def _u16(t):
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def _aligned_by_sort(idx, E, A):
+    T, K = idx.shape
+    ents = sorted((int(idx[t, k]), t, k) for t in range(T) for k in range(K) if 0 <= idx[t, k] < E)
+    cnt = np.bincount([e for e, _, _ in ents], minlength=E)
+    seg = [(-(-c // A)) * A for c in cnt]  # ceil(c / A) * A
+    base = np.concatenate([[0], np.cumsum(seg)])
+    slot = np.full((T, K), -1, np.int64)
+    seen = np.zeros(E, np.int64)
+    for e, t, k in ents:
+        slot[t, k] = base[e] + seen[e]
+        seen[e] += 1
+    src = -np.ones(base[-1], np.int64)
+    for e, t, k in ents:
+        src[slot[t, k]] = t
+    return slot, base, src
+
+
+@pytest.mark.parametrize("T,K,E,A", [(2, 2, 3, 2), (3, 2, 2, 4), (2, 3, 3, 3)])
+def test_alignment_bruteforce(T, K, E, A):
+    vals = list(range(-1, E))
+    for combo in itertools.product(vals, repeat=T * K):
+        idx = np.array(combo, np.int64).reshape(T, K)
+        L = O.layout(idx, E, expert_alignment=A)
+        slot, base, src = _aligned_by_sort(idx, E, A)
+        assert np.array_equal(L["slot"], slot)
+        assert np.array_equal(L["offsets"], base)
+        assert np.array_equal(L["expert_row_src"], src)
+        assert L["n_sel"] == int((idx >= 0).sum())
+        assert L["n_rows_expert"] == base[-1]
+
+
+def test_alignment_one_is_unaligned_and_invariants():
+    w = W.by_name("skewed_masked").replace(T=700)
+    idx, _ = W.make_routing(w)
+    idx = idx.numpy()
+    L0 = O.layout(idx, w.E)
+    L1 = O.layout(idx, w.E, expert_alignment=1)
+    for k in ("counts", "offsets", "slot", "expert_row_src"):
+        assert np.array_equal(L0[k], L1[k])
+    assert L0["n_rows_expert"] == L0["n_sel"]
+    for A in (8, 128):
+        L = O.layout(idx, w.E, expert_alignment=A)
+        off, cnt = L["offsets"], L["counts"]
+        assert np.all(off % A == 0)
+        assert np.all(np.diff(off) == -(-cnt // A) * A)
+        # relative placement inside each segment is the unaligned one
+        for e in range(w.E):
+            sel = idx == e
+            assert np.array_equal(L["slot"][sel] - off[e], L0["slot"][sel] - L0["offsets"][e])
+        # padding rows are exactly the rows past each expert's selections
+        pad = np.ones(L["n_rows_expert"], bool)
+        for e in range(w.E):
+            pad[off[e] : off[e] + cnt[e]] = False
+        assert np.array_equal(L["expert_row_src"] < 0, pad)
+        x = O.bf16_rne(np.random.default_rng(A).standard_normal((w.T, 16)).astype(np.float32))
+        recv = O.dispatch_bf16(x, L["slot"], L["n_rows_expert"])
+        assert not recv[pad].any()
+        assert np.array_equal(recv[~pad], x[L["expert_row_src"][~pad]])
+
+
+def test_bias_masked_token_returns_bias_and_zero_bias_is_no_bias():
+    rng = np.random.default_rng(2)
+    T, H, K = 6, 32, 3
+    y = O.bf16_rne(rng.standard_normal((T * K, H)).astype(np.float32))
+    slot = np.arange(T * K).reshape(T, K)
+    slot[2] = -1
+    slot[4, 1] = -1
+    w = rng.random((T, K)).astype(np.float32)
+    b0 = O.bf16_rne(rng.standard_normal((T, H)).astype(np.float32))
+    b1 = O.bf16_rne(rng.standard_normal((T, H)).astype(np.float32))
+    out1 = O.combine(y, slot, w, bias0=b0)
+    assert np.array_equal(out1[2], b0[2])  # fully masked: its bias, exactly
+    out2 = O.combine(y, slot, w, bias0=b0, bias1=b1)
+    two = (O.bf16_to_f32(b0[2]) + O.bf16_to_f32(b1[2])).astype(np.float32)
+    assert np.array_equal(out2[2], O.bf16_rne(two))
+    zero = np.zeros((T, H), np.uint16)
+    assert np.array_equal(O.combine(y, slot, w, bias0=zero), O.combine(y, slot, w))
+    # float64 reference: bias plus the weighted rows, within bf16 rounding
+    ref = O.bf16_to_f32(b0).astype(np.float64) + O.bf16_to_f32(b1).astype(np.float64)
+    for k in range(K):
+        m = slot[:, k] >= 0
+        ref[m] += w[m, k][:, None].astype(np.float64) * O.bf16_to_f32(y[slot[m, k]]).astype(np.float64)
+    got = O.bf16_to_f32(out2).astype(np.float64)
+    assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0**-8 + 1e-6)
+    # grouped order: the bias seeds the cross-group total
+    idx = np.where(slot >= 0, (np.arange(T * K).reshape(T, K) * 7) % 12, -1)
+    g1 = O.combine_grouped(y, idx, slot, w, 12, 3, bias0=b0)
+    assert np.array_equal(g1[2], b0[2])
+    assert np.array_equal(O.combine_grouped(y, idx, slot, w, 12, 1, bias0=b0, bias1=b1), out2)

@@ -23,7 +23,9 @@ from ._lib import (  # noqa: F401
     EP_ROWS_EXPERT,
     EP_ROWS_GROUP,
     EP_STATUS_COMBINE_OOB,
+    EP_STATUS_EXPERT_LIST_OVERFLOW,
     EP_STATUS_INVALID_IDS,
+    EP_STATUS_SELECTIONS,
     EP_STATUS_LIST_OVERFLOW,
     EP_STATUS_ROWS_EXPERT,
     EP_STATUS_ROWS_GROUP,
@@ -33,6 +35,8 @@ from ._lib import (  # noqa: F401
 
 __all__ = [
     "Layout",
+    "LayoutHandle",
+    "StaleLayoutError",
     "ep_fp8_row_bytes",
     "fp8_row_pitch",
     "ep_layout_workspace_bytes",
@@ -66,8 +70,8 @@ def _stream(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def _problem(T: int, H: int, K: int, E: int, G: int) -> _lib.Problem:
-    return _lib.Problem(T, H, K, E, G)
+def _problem(T: int, H: int, K: int, E: int, G: int, A: int = 0, flags: int = 0) -> _lib.Problem:
+    return _lib.Problem(T, H, K, E, G, A, flags)
 
 
 def ep_fp8_row_bytes(hidden: int) -> int:
@@ -91,9 +95,18 @@ def ep_strerror(code: int) -> str:
     return _lib.lib().ep_strerror(code).decode()
 
 
+class StaleLayoutError(RuntimeError):
+    """A LayoutHandle was used after its Layout's buffers were recomputed."""
+
+
 @dataclasses.dataclass
 class Layout:
-    """Device outputs of ep_layout plus the shape they were computed for."""
+    """Device outputs of ep_layout plus the shape they were computed for.
+
+    ``generation`` counts the ep_layout calls that wrote these buffers; a
+    LayoutHandle taken with ``handle()`` remembers it, so a dispatch replayed
+    from a cached handle is rejected once the buffers hold another routing
+    (the PR's cached ``handle=`` dispatch and its stale-layout guard)."""
 
     num_tokens: int
     topk: int
@@ -111,6 +124,11 @@ class Layout:
     row_topk_weights: torch.Tensor | None = None
     row_capacity: int = 0
     workspace: torch.Tensor | None = None
+    expert_alignment: int = 0
+    expert_row_src: torch.Tensor | None = None
+    expert_row_capacity: int = 0
+    recv_stats: torch.Tensor | None = None
+    generation: int = 0
 
     def struct(self) -> _lib.LayoutStruct:
         return _lib.LayoutStruct(
@@ -125,7 +143,14 @@ class Layout:
             _ptr(self.row_topk_idx),
             _ptr(self.row_topk_weights),
             self.row_capacity,
+            _ptr(self.expert_row_src),
+            self.expert_row_capacity,
+            _ptr(self.recv_stats),
         )
+
+    def max_expert_rows(self) -> int:
+        pad = self.num_experts * (self.expert_alignment - 1) if self.expert_alignment > 1 else 0
+        return self.num_tokens * self.topk + pad
 
     def max_group_rows(self) -> int:
         return min(self.num_tokens * self.num_groups, self.num_tokens * self.topk)
@@ -135,6 +160,29 @@ class Layout:
         w = EP_STATUS_ROWS_EXPERT if rows == EP_ROWS_EXPERT else EP_STATUS_ROWS_GROUP
         return int(self.status[w].item())
 
+    def handle(self) -> "LayoutHandle":
+        return LayoutHandle(self, self.generation)
+
+
+@dataclasses.dataclass(frozen=True)
+class LayoutHandle:
+    """A Layout as it was at one generation (see Layout)."""
+
+    layout: Layout
+    generation: int
+
+    def get(self) -> Layout:
+        if self.layout.generation != self.generation:
+            raise StaleLayoutError(
+                f"layout recomputed since this handle was taken (generation {self.generation} -> "
+                f"{self.layout.generation})"
+            )
+        return self.layout
+
+
+def _resolve(layout) -> Layout:
+    return layout.get() if isinstance(layout, LayoutHandle) else layout
+
 
 def ep_layout(
     topk_idx: torch.Tensor,
@@ -143,24 +191,43 @@ def ep_layout(
     topk_weights: torch.Tensor | None = None,
     row_capacity: int | None = None,
     out: Layout | None = None,
+    expert_alignment: int = 0,
+    expert_row_src: bool = False,
+    recv_stats: torch.Tensor | None = None,
 ) -> Layout:
     """Count, scan and place every selection of topk_idx (int64 [T, K]).
 
-    ``out`` reuses the buffers of an earlier Layout of the same shape
-    (nothing is allocated then)."""
+    ``expert_alignment`` rounds each expert segment up to a multiple of that
+    many rows; ``expert_row_src`` also returns each expert-major row's source
+    token (-1 on padding rows); ``recv_stats`` (uint32 as int32 [E]) gets the
+    per-expert counts added to it.  ``out`` reuses the buffers of an earlier
+    Layout of the same shape (nothing is allocated then; its generation
+    advances)."""
     if topk_idx.dim() != 2:
         raise ValueError("topk_idx must be [T, K]")
     T, K = topk_idx.shape
     _dev(topk_idx, "topk_idx", torch.int64)
     dev = topk_idx.device
     G = int(num_groups)
+    A = int(expert_alignment)
     if topk_weights is not None:
         _dev(topk_weights, "topk_weights", torch.float32, (T, K))
+    if recv_stats is not None:
+        if recv_stats.dtype not in (torch.int32, torch.uint32):
+            raise TypeError("recv_stats must be a 32-bit integer tensor")
+        _dev(recv_stats, "recv_stats", recv_stats.dtype, (num_experts,))
     if out is not None:
-        if (out.num_tokens, out.topk, out.num_experts, out.num_groups) != (T, K, num_experts, G):
+        if (out.num_tokens, out.topk, out.num_experts, out.num_groups, out.expert_alignment) != (
+            T,
+            K,
+            num_experts,
+            G,
+            A,
+        ):
             raise ValueError("out was allocated for a different problem shape")
         if G > 0 and topk_weights is None:
             raise ValueError("grouped layout needs topk_weights for the per-row weight lists")
+        out.recv_stats = recv_stats
         _run_layout(out, topk_idx, topk_weights)
         return out
     i32 = dict(dtype=torch.int32, device=dev)
@@ -173,7 +240,12 @@ def ep_layout(
         offsets=torch.empty(num_experts + 1, **i32),
         slot=torch.empty(T, K, **i32),
         status=torch.empty(_lib.EP_STATUS_WORDS, **i32),
+        expert_alignment=A,
+        recv_stats=recv_stats,
     )
+    if expert_row_src:
+        L.expert_row_capacity = L.max_expert_rows()
+        L.expert_row_src = torch.empty(max(L.expert_row_capacity, 1), **i32)
     if G > 0:
         cap = L.max_group_rows() if row_capacity is None else int(row_capacity)
         L.row_capacity = cap
@@ -185,7 +257,7 @@ def ep_layout(
         L.row_topk_weights = torch.empty(max(cap, 1), K, dtype=torch.float32, device=dev)
         if topk_weights is None:
             raise ValueError("grouped layout needs topk_weights for the per-row weight lists")
-    p = _problem(T, 1, K, num_experts, G)
+    p = _problem(T, 1, K, num_experts, G, A)
     nbytes = int(_lib.lib().ep_layout_workspace_bytes(ctypes.byref(p)))
     if nbytes == 0:
         raise _lib.EPError("ep_layout_workspace_bytes", _lib.EP_EINVAL, "invalid problem shape")
@@ -195,7 +267,7 @@ def ep_layout(
 
 
 def _run_layout(L: Layout, topk_idx: torch.Tensor, topk_weights: torch.Tensor | None) -> None:
-    p = _problem(L.num_tokens, 1, L.topk, L.num_experts, L.num_groups)
+    p = _problem(L.num_tokens, 1, L.topk, L.num_experts, L.num_groups, L.expert_alignment)
     s = L.struct()
     rc = _lib.lib().ep_layout(
         ctypes.byref(p),
@@ -207,6 +279,7 @@ def _run_layout(L: Layout, topk_idx: torch.Tensor, topk_weights: torch.Tensor | 
         _stream(topk_idx.device),
     )
     _lib.check("ep_layout", rc)
+    L.generation += 1
 
 
 def ep_dispatch(
@@ -217,6 +290,7 @@ def ep_dispatch(
     capacity: int | None = None,
     out: torch.Tensor | None = None,
     row_stride: int | None = None,
+    zero_padding: bool = False,
 ) -> torch.Tensor:
     """Scatter token rows x (bf16 [T, H]) to their receive rows.
 
@@ -226,13 +300,16 @@ def ep_dispatch(
     ``row_stride`` bytes (default: the row size, rows packed back to back).
     Only the first row-size bytes of each row are written.  The default
     capacity is the worst case (T*K expert rows, min(T*G, T*K) group rows),
-    so no host synchronisation is needed."""
+    so no host synchronisation is needed.  ``layout`` may be a LayoutHandle
+    (checked against its generation).  ``zero_padding`` also zeroes the
+    expert alignment padding rows."""
+    layout = _resolve(layout)
     if x.dim() != 2 or x.shape[0] != layout.num_tokens:
         raise ValueError("x must be [T, H] with the layout's T")
     _dev(x, "x", torch.bfloat16)
     T, H = x.shape
     if capacity is None:
-        capacity = T * layout.topk if rows == EP_ROWS_EXPERT else layout.max_group_rows()
+        capacity = layout.max_expert_rows() if rows == EP_ROWS_EXPERT else layout.max_group_rows()
     fmt = EP_FORMAT_FP8_PACKED if fp8 else EP_FORMAT_BF16
     if fp8:
         rb = ep_fp8_row_bytes(H)
@@ -254,7 +331,8 @@ def ep_dispatch(
         if row_stride is not None and row_stride != out.shape[1] * esize:
             raise ValueError("row_stride disagrees with out's row size")
     pitch = out.shape[1] * esize
-    p = _problem(T, H, layout.topk, layout.num_experts, layout.num_groups)
+    flags = _lib.EP_FLAG_ZERO_PADDING if zero_padding else 0
+    p = _problem(T, H, layout.topk, layout.num_experts, layout.num_groups, layout.expert_alignment, flags)
     s = layout.struct()
     rc = _lib.lib().ep_dispatch(
         ctypes.byref(p),
@@ -278,9 +356,13 @@ def ep_combine(
     topk_idx: torch.Tensor | None = None,
     order: int = EP_COMBINE_FLAT,
     out: torch.Tensor | None = None,
+    bias0: torch.Tensor | None = None,
+    bias1: torch.Tensor | None = None,
 ) -> torch.Tensor:
     """Weighted reduction of each token's expert-output rows y (bf16 [rows, H],
-    expert-major) into out (bf16 [T, H])."""
+    expert-major) into out (bf16 [T, H]); bias0 / bias1 (bf16 [T, H]) seed the
+    accumulator."""
+    layout = _resolve(layout)
     if y.dim() != 2:
         raise ValueError("y must be [rows, H]")
     _dev(y, "y", torch.bfloat16)
@@ -291,11 +373,14 @@ def ep_combine(
         _dev(topk_idx, "topk_idx", torch.int64, (T, K))
     if order == EP_COMBINE_GROUPED and topk_idx is None:
         raise ValueError("grouped order needs topk_idx")
+    for name, b in (("bias0", bias0), ("bias1", bias1)):
+        if b is not None:
+            _dev(b, name, torch.bfloat16, (T, H))
     if out is None:
         out = torch.empty(T, H, dtype=torch.bfloat16, device=y.device)
     else:
         _dev(out, "out", torch.bfloat16, (T, H))
-    p = _problem(T, H, K, layout.num_experts, layout.num_groups)
+    p = _problem(T, H, K, layout.num_experts, layout.num_groups, layout.expert_alignment)
     s = layout.struct()
     rc = _lib.lib().ep_combine(
         ctypes.byref(p),
@@ -304,6 +389,8 @@ def ep_combine(
         _ptr(topk_weights),
         _ptr(y),
         int(y.shape[0]),
+        _ptr(bias0),
+        _ptr(bias1),
         _ptr(out),
         int(order),
         _stream(y.device),

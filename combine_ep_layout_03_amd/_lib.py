@@ -26,7 +26,11 @@ EP_STATUS_ROWS_EXPERT = 1
 EP_STATUS_ROWS_GROUP = 2
 EP_STATUS_LIST_OVERFLOW = 3
 EP_STATUS_COMBINE_OOB = 4
+EP_STATUS_EXPERT_LIST_OVERFLOW = 5
+EP_STATUS_SELECTIONS = 6
 EP_STATUS_WORDS = 8
+
+EP_FLAG_ZERO_PADDING = 1
 
 EP_FORMAT_BF16 = 0
 EP_FORMAT_FP8_PACKED = 1
@@ -52,6 +56,8 @@ class Problem(ctypes.Structure):
         ("topk", ctypes.c_int32),
         ("num_experts", ctypes.c_int32),
         ("num_groups", ctypes.c_int32),
+        ("expert_alignment", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
     ]
 
 
@@ -68,6 +74,9 @@ class LayoutStruct(ctypes.Structure):
         ("row_topk_idx", ctypes.c_void_p),
         ("row_topk_weights", ctypes.c_void_p),
         ("row_capacity", ctypes.c_int64),
+        ("expert_row_src", ctypes.c_void_p),
+        ("expert_row_capacity", ctypes.c_int64),
+        ("recv_stats", ctypes.c_void_p),
     ]
 
 
@@ -102,7 +111,7 @@ def lib(path: str | None = None) -> ctypes.CDLL:
     L.ep_layout.restype = ctypes.c_int
     L.ep_dispatch.argtypes = [P, LS, vp, vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, vp]
     L.ep_dispatch.restype = ctypes.c_int
-    L.ep_combine.argtypes = [P, LS, vp, vp, vp, ctypes.c_int64, vp, ctypes.c_int32, vp]
+    L.ep_combine.argtypes = [P, LS, vp, vp, vp, ctypes.c_int64, vp, vp, vp, ctypes.c_int32, vp]
     L.ep_combine.restype = ctypes.c_int
     L.ep_strerror.argtypes = [ctypes.c_int]
     L.ep_strerror.restype = ctypes.c_char_p

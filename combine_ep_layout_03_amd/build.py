@@ -19,6 +19,10 @@ LIB_PATH = os.path.join(HERE, LIB_NAME)
 
 SOURCES = ["ep_api.hip", "ep_layout.hip", "ep_dispatch.hip", "ep_combine.hip"]
 
+# test-only library exposing the device E4M3FN encoders (tests/hip)
+TEST_SOURCE = os.path.join(ROOT, "tests", "hip", "e4m3_check.hip")
+TEST_LIB_PATH = os.path.join(ROOT, "tests", "hip", "libep_e4m3_check.so")
+
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
@@ -58,5 +62,19 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None, out: str 
     return out
 
 
+def build_test_lib(verbose: bool = False) -> str:
+    """Compile the test-only encoder library with the product's flags."""
+    tmp = TEST_LIB_PATH + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, TEST_SOURCE, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, TEST_LIB_PATH)
+    return TEST_LIB_PATH
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_test_lib(verbose=True))

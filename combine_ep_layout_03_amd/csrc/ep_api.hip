@@ -17,10 +17,14 @@ int check_problem(const ep_problem_t* p) {
       p->num_groups < 0)
     return EP_EINVAL;
   if (p->num_groups > 0 && p->num_experts % p->num_groups != 0) return EP_EINVAL;
+  if (p->expert_alignment < 0 || p->expert_alignment > (1 << 20)) return EP_EINVAL;
+  if (p->flags & ~EP_FLAG_ZERO_PADDING) return EP_EINVAL;
   if (p->topk > EP_MAX_TOPK) return EP_ENOTSUP;
   if (static_cast<int64_t>(p->num_experts) + p->num_groups > EP_MAX_KEYS) return EP_ENOTSUP;
-  // slots and rows are int32: every (t,k) must index below 2^31
-  if (p->num_tokens > static_cast<int64_t>(INT32_MAX) / p->topk) return EP_ENOTSUP;
+  // slots and rows are int32: every (t,k) row, padding included, must index below 2^31
+  const int64_t pad = static_cast<int64_t>(p->num_experts) *
+                      (p->expert_alignment > 1 ? p->expert_alignment - 1 : 0);
+  if (p->num_tokens > (static_cast<int64_t>(INT32_MAX) - pad) / p->topk) return EP_ENOTSUP;
   return EP_OK;
 }
 
@@ -64,6 +68,7 @@ int ep_layout(const ep_problem_t* p, const int64_t* topk_idx, const float* topk_
         (!L->row_src || !L->row_topk_idx || !L->row_topk_weights || !topk_weights))
       return EP_EINVAL;
   }
+  if (L->expert_row_src && L->expert_row_capacity < 0) return EP_EINVAL;
   if (!aligned(topk_idx, 8) || !aligned(workspace, 4)) return EP_EINVAL;
 
   const ep::LayoutGeom g = ep::layout_geom(T * p->topk, p->num_experts, p->num_groups);
@@ -88,6 +93,10 @@ int ep_layout(const ep_problem_t* p, const int64_t* topk_idx, const float* topk_
   a.row_idx = L->row_topk_idx;
   a.row_w = L->row_topk_weights;
   a.row_cap = grouped ? L->row_capacity : 0;
+  a.align = p->expert_alignment > 1 ? p->expert_alignment : 1;
+  a.expert_row_src = L->expert_row_src;
+  a.expert_row_cap = L->expert_row_src ? L->expert_row_capacity : 0;
+  a.recv_stats = L->recv_stats;
   a.partials = static_cast<int32_t*>(workspace);
   return ep::launch_layout(a, g, stream) == hipSuccess ? EP_OK : EP_EHIP;
 }
@@ -124,21 +133,29 @@ int ep_dispatch(const ep_problem_t* p, const ep_layout_t* L, const void* x, void
   a.capacity = capacity_rows;
   a.stride = stride;
   a.dedup = rows == EP_ROWS_GROUP;
+  a.counts = L->counts;
+  a.offsets = L->offsets;
+  a.E = p->num_experts;
+  const bool zero_pad =
+      (p->flags & EP_FLAG_ZERO_PADDING) && rows == EP_ROWS_EXPERT && p->expert_alignment > 1;
+  if (zero_pad && (!L->counts || !L->offsets)) return EP_EINVAL;
   hipError_t err;
+  int vb = 16;
   if (format == EP_FORMAT_FP8_PACKED) {
     if (!aligned(x, 16) || !aligned(recv, 16) || stride % 16 != 0) return EP_EINVAL;
     err = ep::launch_scatter_fp8(a, row_bytes, stream);
   } else {
-    int vb = vec_bytes_for(row_bytes, x, recv);
+    vb = vec_bytes_for(row_bytes, x, recv);
     while (stride % vb != 0) vb >>= 1;
     err = ep::launch_scatter_bf16(a, vb, stream);
   }
+  if (err == hipSuccess && zero_pad) err = ep::launch_zero_padding(a, row_bytes, vb, stream);
   return err == hipSuccess ? EP_OK : EP_EHIP;
 }
 
 int ep_combine(const ep_problem_t* p, const ep_layout_t* L, const int64_t* topk_idx,
-               const float* topk_weights, const void* y, int64_t y_rows, void* out,
-               int32_t order, hipStream_t stream) {
+               const float* topk_weights, const void* y, int64_t y_rows, const void* bias0,
+               const void* bias1, void* out, int32_t order, hipStream_t stream) {
   int rc = check_problem(p);
   if (rc != EP_OK) return rc;
   if (!L || !L->status || y_rows < 0) return EP_EINVAL;
@@ -149,7 +166,7 @@ int ep_combine(const ep_problem_t* p, const ep_layout_t* L, const int64_t* topk_
   if (!L->slot || !topk_weights || !out || (grouped && !topk_idx)) return EP_EINVAL;
   if (!y && y_rows > 0) return EP_EINVAL;
   if (!aligned(y, 2) || !aligned(out, 2) || !aligned(topk_weights, 4) ||
-      !aligned(topk_idx, 8))
+      !aligned(topk_idx, 8) || !aligned(bias0, 2) || !aligned(bias1, 2))
     return EP_EINVAL;
 
   ep::CombineArgs a;
@@ -163,10 +180,13 @@ int ep_combine(const ep_problem_t* p, const ep_layout_t* L, const int64_t* topk_
   a.T = p->num_tokens;
   a.K = p->topk;
   a.H = p->hidden;
+  a.bias0 = bias0;
+  a.bias1 = bias1;
   a.out = out;
   a.status = L->status;
   a.grouped = grouped;
-  const int ve = vec_bytes_for(static_cast<int64_t>(p->hidden) * 2, y ? y : out, out) / 2;
+  int ve = vec_bytes_for(static_cast<int64_t>(p->hidden) * 2, y ? y : out, out) / 2;
+  while (ve > 1 && (!aligned(bias0, 2 * ve) || !aligned(bias1, 2 * ve))) ve >>= 1;
   return ep::launch_combine(a, ve, stream) == hipSuccess ? EP_OK : EP_EHIP;
 }
 

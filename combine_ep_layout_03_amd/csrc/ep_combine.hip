@@ -10,7 +10,10 @@
 // group partials in ascending group order, as the expanded combine sums a
 // token's local-expert rows before one row per destination is sent (commit
 // adding kDoExpandedSend).  Masked entries (-1) are skipped, so a fully
-// masked token gives +0 (commit on masked topk_idx).
+// masked token gives +0 (commit on masked topk_idx).  An optional bias (one
+// or two bf16 rows per token) seeds the accumulator instead of +0, so a fully
+// masked token returns its bias (commit adding receive stats and combine
+// bias); in the grouped order it seeds the cross-group total.
 //
 // Work split: a token row is cut into chunks of 64*U vectors; the
 // persistent grid's waves take contiguous ranges of (token, chunk) items, so
@@ -123,17 +126,39 @@ __device__ __forceinline__ void load_sel(const CombineArgs& a, int64_t t, int la
   }
 }
 
+// The accumulator's starting value for element e of a vector: +0, or the
+// bias (one or two bf16 rows, summed in fp32).
+template <int VE, int NB>
+__device__ __forceinline__ float bias_seed(const typename BfVec<VE>::V (&b)[2], int e) {
+  using B = BfVec<VE>;
+  if (NB == 0) return 0.0f;
+  if (NB == 1) return B::get(b[0], e);
+  return __fadd_rn(B::get(b[0], e), B::get(b[1], e));
+}
+
+template <int VE, int NB>
+__device__ __forceinline__ void load_bias(const CombineArgs& a, int64_t t, int nvec, int vi,
+                                          typename BfVec<VE>::V (&b)[2]) {
+  using V = typename BfVec<VE>::V;
+  const int64_t off = t * nvec + vi;
+  b[0] = NB >= 1 ? static_cast<const V*>(a.bias0 ? a.bias0 : a.bias1)[off] : V{};
+  b[1] = NB >= 2 ? static_cast<const V*>(a.bias1)[off] : V{};
+}
+
 // One chunk: U vectors per lane of the token's output row.
-template <int KMAX, int VE, bool GROUPED, int U, bool FULL>
-__device__ __forceinline__ void reduce_chunk(const typename BfVec<VE>::V* __restrict__ yv,
+template <int KMAX, int VE, bool GROUPED, int U, bool FULL, int NB>
+__device__ __forceinline__ void reduce_chunk(const CombineArgs& a, int64_t t,
+                                             const typename BfVec<VE>::V* __restrict__ yv,
                                              typename BfVec<VE>::V* __restrict__ outv, int nvec,
                                              int vb, int lane, const Sel<KMAX>& m) {
   using B = BfVec<VE>;
   using V = typename B::V;
   V in[U][KMAX];
+  V bias[U][2];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int vi = min(vb + u * kWave + lane, nvec - 1);
+    if (NB > 0) load_bias<VE, NB>(a, t, nvec, vi, bias[u]);
 #pragma unroll
     for (int i = 0; i < KMAX; ++i) in[u][i] = nt_load(yv + static_cast<int64_t>(m.os[i]) * nvec + vi);
   }
@@ -142,7 +167,9 @@ __device__ __forceinline__ void reduce_chunk(const typename BfVec<VE>::V* __rest
     float res[VE];
 #pragma unroll
     for (int e = 0; e < VE; ++e) {
-      float tot = 0.0f, P = 0.0f;
+      // flat: acc = seed, then acc += w*y;  grouped: tot = seed, P per group
+      float tot = bias_seed<VE, NB>(bias[u], e);
+      float P = GROUPED ? 0.0f : tot;
 #pragma unroll
       for (int i = 0; i < KMAX; ++i) {
         if (FULL || i < m.nv) {
@@ -160,7 +187,31 @@ __device__ __forceinline__ void reduce_chunk(const typename BfVec<VE>::V* __rest
   }
 }
 
-template <int KMAX, int VE, bool GROUPED, int U>
+// A token with no valid selection: the bias seed (grouped: seed + 0, as the
+// cross-group total adds the empty partials), or +0 without a bias.
+template <int VE, bool GROUPED, int U, int NB>
+__device__ __forceinline__ void empty_chunk(const CombineArgs& a, int64_t t,
+                                            typename BfVec<VE>::V* __restrict__ outv, int nvec,
+                                            int vb, int lane) {
+  using B = BfVec<VE>;
+  using V = typename B::V;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int vi = vb + u * kWave + lane;
+    if (vi >= nvec) continue;
+    V bias[2];
+    if (NB > 0) load_bias<VE, NB>(a, t, nvec, vi, bias);
+    float res[VE];
+#pragma unroll
+    for (int e = 0; e < VE; ++e) {
+      const float seed = bias_seed<VE, NB>(bias, e);
+      res[e] = GROUPED ? __fadd_rn(seed, 0.0f) : seed;
+    }
+    outv[vi] = B::pack(res);
+  }
+}
+
+template <int KMAX, int VE, bool GROUPED, int U, int NB>
 __global__ __launch_bounds__(kBlock) void k_combine(CombineArgs a, int nchunks, int64_t items) {
   using B = BfVec<VE>;
   using V = typename B::V;
@@ -183,39 +234,42 @@ __global__ __launch_bounds__(kBlock) void k_combine(CombineArgs a, int nchunks, 
     V* outv = static_cast<V*>(a.out) + t * nvec;
     const int vb = c * (kWave * U);
     if (m.nv == KMAX) {
-      reduce_chunk<KMAX, VE, GROUPED, U, true>(yv, outv, nvec, vb, lane, m);
+      reduce_chunk<KMAX, VE, GROUPED, U, true, NB>(a, t, yv, outv, nvec, vb, lane, m);
     } else if (m.nv > 0) {
-      reduce_chunk<KMAX, VE, GROUPED, U, false>(yv, outv, nvec, vb, lane, m);
+      reduce_chunk<KMAX, VE, GROUPED, U, false, NB>(a, t, yv, outv, nvec, vb, lane, m);
     } else {
-      const float zf[VE] = {};
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int vi = vb + u * kWave + lane;
-        if (vi < nvec) outv[vi] = B::pack(zf);
-      }
+      empty_chunk<VE, GROUPED, U, NB>(a, t, outv, nvec, vb, lane);
     }
   }
 }
 
-template <int KMAX, int VE, bool GROUPED>
+template <int KMAX, int VE, bool GROUPED, int NB>
 hipError_t combine_v(const CombineArgs& a, hipStream_t s) {
   // two row chunks in flight per lane while the K loads stay within registers
   constexpr int U = KMAX <= 8 ? 2 : 1;
   const int nvec = a.H / VE;
   const int nchunks = (nvec + kWave * U - 1) / (kWave * U);
   const int64_t items = a.T * nchunks;
-  constexpr auto kern = k_combine<KMAX, VE, GROUPED, U>;
+  constexpr auto kern = k_combine<KMAX, VE, GROUPED, U, NB>;
   kern<<<persistent_blocks<kern>(items), kBlock, 0, s>>>(a, nchunks, items);
   return hipGetLastError();
+}
+
+template <int KMAX, int VE, bool GROUPED>
+hipError_t combine_b(const CombineArgs& a, hipStream_t s) {
+  const int nb = (a.bias0 ? 1 : 0) + (a.bias1 ? 1 : 0);
+  if (nb == 0) return combine_v<KMAX, VE, GROUPED, 0>(a, s);
+  if (nb == 1) return combine_v<KMAX, VE, GROUPED, 1>(a, s);
+  return combine_v<KMAX, VE, GROUPED, 2>(a, s);
 }
 
 template <int KMAX, bool GROUPED>
 hipError_t combine_k(const CombineArgs& a, int ve, hipStream_t s) {
   switch (ve) {
-    case 8: return combine_v<KMAX, 8, GROUPED>(a, s);
-    case 4: return combine_v<KMAX, 4, GROUPED>(a, s);
-    case 2: return combine_v<KMAX, 2, GROUPED>(a, s);
-    default: return combine_v<KMAX, 1, GROUPED>(a, s);
+    case 8: return combine_b<KMAX, 8, GROUPED>(a, s);
+    case 4: return combine_b<KMAX, 4, GROUPED>(a, s);
+    case 2: return combine_b<KMAX, 2, GROUPED>(a, s);
+    default: return combine_b<KMAX, 1, GROUPED>(a, s);
   }
 }
 

@@ -173,6 +173,27 @@ __global__ __launch_bounds__(kBlock) void k_scatter_fp8(ScatterArgs a, int64_t r
   }
 }
 
+// Zero the alignment padding rows [offsets[e] + counts[e], offsets[e+1]) of
+// every expert: the PR's zero_padding, so each expert's A-aligned block
+// holds its rows followed by zeros.  Blocks take experts in turn.
+template <int VB>
+__global__ __launch_bounds__(kBlock) void k_zero_padding(ScatterArgs a, int64_t row_bytes) {
+  using V = typename VecOf<VB>::type;
+  if (static_cast<int64_t>(*a.rows_needed) > a.capacity) return;
+  const int nvec = static_cast<int>(row_bytes / VB);
+  char* rbase = static_cast<char*>(a.recv);
+  for (int e = blockIdx.x; e < a.E; e += gridDim.x) {
+    const int r0 = a.offsets[e] + a.counts[e];
+    const int r1 = a.offsets[e + 1];
+    const int64_t n = static_cast<int64_t>(r1 - r0) * nvec;
+    for (int64_t q = threadIdx.x; q < n; q += kBlock) {
+      const int64_t r = r0 + q / nvec;
+      const int v = static_cast<int>(q % nvec);
+      nt_store(V{}, reinterpret_cast<V*>(rbase + r * a.stride) + v);
+    }
+  }
+}
+
 template <int KMAX, int VB>
 hipError_t scatter_bf16_v(const ScatterArgs& a, hipStream_t s) {
   constexpr int U = 4;
@@ -210,6 +231,18 @@ hipError_t launch_scatter_bf16(const ScatterArgs& a, int vec_bytes, hipStream_t 
   if (a.K <= 8) return scatter_bf16_k<8>(a, vec_bytes, s);
   if (a.K <= 16) return scatter_bf16_k<16>(a, vec_bytes, s);
   return scatter_bf16_k<32>(a, vec_bytes, s);
+}
+
+hipError_t launch_zero_padding(const ScatterArgs& a, int64_t row_bytes, int vec_bytes,
+                               hipStream_t s) {
+  const unsigned grid = static_cast<unsigned>(a.E < 1024 ? a.E : 1024);
+  switch (vec_bytes) {
+    case 16: k_zero_padding<16><<<grid, kBlock, 0, s>>>(a, row_bytes); break;
+    case 8: k_zero_padding<8><<<grid, kBlock, 0, s>>>(a, row_bytes); break;
+    case 4: k_zero_padding<4><<<grid, kBlock, 0, s>>>(a, row_bytes); break;
+    default: k_zero_padding<2><<<grid, kBlock, 0, s>>>(a, row_bytes); break;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_scatter_fp8(const ScatterArgs& a, int64_t row_bytes, hipStream_t s) {

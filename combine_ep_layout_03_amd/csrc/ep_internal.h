@@ -34,6 +34,10 @@ struct LayoutArgs {
   int32_t* row_idx;
   float* row_w;
   int64_t row_cap;
+  int align;  // expert segment alignment (1 = none)
+  int32_t* expert_row_src;  // optional
+  int64_t expert_row_cap;
+  uint32_t* recv_stats;  // optional, accumulated
   int32_t* partials;  // workspace
 };
 hipError_t launch_layout(const LayoutArgs& a, const LayoutGeom& g, hipStream_t s);
@@ -49,12 +53,20 @@ struct ScatterArgs {
   int64_t capacity;
   int64_t stride;  // bytes from one receive row to the next
   bool dedup;  // several k may name one row (grouped rows)
+  // alignment padding rows to zero (expert rows only): [offsets[e] + counts[e], offsets[e+1])
+  const int32_t* counts;
+  const int32_t* offsets;
+  int E;
 };
 // bf16 rows; `vec_bytes` in {16, 8, 4, 2} divides the row size, the stride
 // and both base alignments.
 hipError_t launch_scatter_bf16(const ScatterArgs& a, int vec_bytes, hipStream_t s);
 // packed fp8 rows; H % 128 == 0, H <= 32768, 16-byte aligned bases and stride.
 hipError_t launch_scatter_fp8(const ScatterArgs& a, int64_t row_bytes, hipStream_t s);
+// zero the first row_bytes bytes of every alignment padding row; `vec_bytes`
+// divides row_bytes, the stride and the base alignment.
+hipError_t launch_zero_padding(const ScatterArgs& a, int64_t row_bytes, int vec_bytes,
+                               hipStream_t s);
 
 struct CombineArgs {
   const void* y;
@@ -67,6 +79,8 @@ struct CombineArgs {
   int64_t T;
   int K;
   int H;
+  const void* bias0;  // optional bf16 [T*H]
+  const void* bias1;  // optional bf16 [T*H]
   void* out;
   int32_t* status;
   bool grouped;

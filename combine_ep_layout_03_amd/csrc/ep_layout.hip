@@ -169,19 +169,26 @@ __global__ __launch_bounds__(kBlock) void k_layout_place(LayoutArgs a, int ncols
   // the first round's id, loaded early so its latency overlaps the scans
   int64_t v_next = (base + tid < a.n) ? a.idx[base + tid] : -1;
 
-  // Segment bases: exclusive prefix sums of the totals, over the experts and
-  // (separately) over the groups.
-  for (int c = tid; c < nkeys; c += kBlock) sbase[c] = tot[c];
+  // Segment bases: exclusive prefix sums over the experts of their counts
+  // rounded up to the alignment, and (separately) over the groups.  The raw
+  // expert counts are scanned too, for the number of selections.
+  const int A = a.align;
+  for (int c = tid; c < E; c += kBlock) run[c] = tot[c];
+  for (int c = tid; c < nkeys; c += kBlock) sbase[c] = c < E ? (tot[c] + A - 1) / A * A : tot[c];
   __syncthreads();
-  const int n_sel = block_exclusive_scan(sbase, E, tmp);
+  const int n_sel = A > 1 ? block_exclusive_scan(run, E, tmp) : 0;
+  const int n_rows_e = block_exclusive_scan(sbase, E, tmp);
   int n_rows = 0;
   if (GROUPED) n_rows = block_exclusive_scan(sbase + E, a.G, tmp);
   const bool lists_ok = !GROUPED || static_cast<int64_t>(n_rows) <= a.row_cap;
+  const bool erows_ok =
+      a.expert_row_src != nullptr && static_cast<int64_t>(n_rows_e) <= a.expert_row_cap;
 
   if (blockIdx.x == 0) {
     for (int e = tid; e < E; e += kBlock) {
       a.counts[e] = tot[e];
       a.offsets[e] = sbase[e];
+      if (a.recv_stats) a.recv_stats[e] += static_cast<uint32_t>(tot[e]);
     }
     if (GROUPED) {
       for (int g = tid; g < a.G; g += kBlock) {
@@ -190,15 +197,28 @@ __global__ __launch_bounds__(kBlock) void k_layout_place(LayoutArgs a, int ncols
       }
     }
     if (tid == 0) {
-      a.offsets[E] = n_sel;
+      a.offsets[E] = n_rows_e;
       if (GROUPED) a.goffsets[a.G] = n_rows;
       a.status[0] = tot[ncols - 1];
-      a.status[1] = n_sel;
+      a.status[1] = n_rows_e;
       a.status[2] = n_rows;
       a.status[3] = lists_ok ? 0 : 1;
-      for (int s = 4; s < 8; ++s) a.status[s] = 0;
+      a.status[4] = 0;
+      a.status[5] = (a.expert_row_src != nullptr && !erows_ok) ? 1 : 0;
+      a.status[6] = A > 1 ? n_sel : n_rows_e;
+      a.status[7] = 0;
     }
   }
+  // alignment padding rows are marked unoccupied (-1); experts are spread
+  // over the blocks
+  if (A > 1 && erows_ok) {
+    for (int e = blockIdx.x; e < E; e += gridDim.x) {
+      const int r0 = sbase[e] + tot[e];
+      const int r1 = sbase[e] + (tot[e] + A - 1) / A * A;
+      for (int r = r0 + tid; r < r1; r += kBlock) a.expert_row_src[r] = -1;
+    }
+  }
+  __syncthreads();  // run[] is reused below
 
   // This block's base per key: segment base + entries of earlier blocks.
   const int* mine = a.partials + static_cast<size_t>(blockIdx.x) * ncols;
@@ -254,6 +274,7 @@ __global__ __launch_bounds__(kBlock) void k_layout_place(LayoutArgs a, int ncols
       }
     }
     if (in) a.slot[i] = e >= 0 ? sbase[e] + rankE : -1;
+    if (erows_ok && e >= 0) a.expert_row_src[sbase[e] + rankE] = static_cast<int>(i / static_cast<uint32_t>(a.K));
     if (GROUPED && in) {
       if (!valid) a.grow[i] = -1;
       if (kg >= 0) {

@@ -57,11 +57,16 @@ extern "C" {
 
 /* ---- device status words written by ep_layout ------------------------ */
 #define EP_STATUS_INVALID_IDS 0 /* ids outside {-1} U [0,E): counted, treated as -1 */
-#define EP_STATUS_ROWS_EXPERT 1 /* N_sel: rows of the expert-major layout */
+#define EP_STATUS_ROWS_EXPERT 1 /* rows of the expert-major layout (selections + padding) */
 #define EP_STATUS_ROWS_GROUP 2  /* R: rows of the grouped layout (0 without groups) */
 #define EP_STATUS_LIST_OVERFLOW 3 /* 1 if R > row_capacity: row lists not written */
 #define EP_STATUS_COMBINE_OOB 4 /* set to 1 by ep_combine if a slot >= y_rows was met */
+#define EP_STATUS_EXPERT_LIST_OVERFLOW 5 /* 1 if expert rows > expert_row_capacity */
+#define EP_STATUS_SELECTIONS 6  /* valid selections (EP_STATUS_ROWS_EXPERT minus padding) */
 #define EP_STATUS_WORDS 8
+
+/* ---- problem flags ---------------------------------------------------- */
+#define EP_FLAG_ZERO_PADDING 1 /* dispatch zeroes the alignment padding rows */
 
 /* ---- formats, row kinds, combine orders ------------------------------ */
 #define EP_FORMAT_BF16 0       /* receive row = the token's H bf16 values */
@@ -82,22 +87,42 @@ extern "C" {
  *               experts also form G contiguous groups of E/G (a group plays
  *               the role of a destination rank) and the layout adds one
  *               deduplicated row per (token, group hit).  E + G must not
- *               exceed EP_MAX_KEYS. */
+ *               exceed EP_MAX_KEYS.
+ *   expert_alignment  0 or 1 = none; A >= 2 rounds every expert segment of
+ *               the expert-major layout up to a multiple of A rows, so each
+ *               expert's rows form an A-aligned block a grouped GEMM can
+ *               consume (PR commit adding do_expand: expert_alignment).  The
+ *               rows past an expert's selections are padding.
+ *   flags       EP_FLAG_ZERO_PADDING: ep_dispatch also zeroes every byte of
+ *               the padding rows' row size (the PR's zero_padding). */
 typedef struct ep_problem {
   int64_t num_tokens;
   int32_t hidden;
   int32_t topk;
   int32_t num_experts;
   int32_t num_groups;
+  int32_t expert_alignment;
+  int32_t flags;
 } ep_problem_t;
 
 /* Layout outputs: device pointers, caller-owned, all int32 unless noted.
  *   counts[E]          selections per expert
- *   offsets[E+1]       exclusive prefix sum of counts; offsets[E] = N_sel
+ *   offsets[E+1]       exclusive prefix sum of the (aligned) counts;
+ *                      offsets[E] = rows of the expert-major layout
  *   slot[T*K]          expert-major row of (t,k): offsets[e] + number of
  *                      earlier (t',k') in (t,k) order with the same expert;
  *                      -1 for masked or invalid entries
  *   status[EP_STATUS_WORDS]
+ *   expert_row_src[expert_row_capacity]   optional (NULL = not written):
+ *                      source token of each expert-major row, -1 for an
+ *                      alignment padding row (marked unoccupied); not
+ *                      written if the rows exceed the capacity
+ *                      (EP_STATUS_EXPERT_LIST_OVERFLOW)
+ *   recv_stats[E]      optional uint32 (NULL = not touched): counts[e] is
+ *                      ADDED to recv_stats[e], so the caller chooses the
+ *                      accumulation window by when it clears it (the PR's
+ *                      cumulative_local_expert_recv_stats, commit adding
+ *                      receive stats and combine bias)
  * Grouped layout (only read/written when num_groups >= 1; may be NULL otherwise):
  *   group_counts[G], group_offsets[G+1]   rows per group and their prefix sum
  *   grow[T*K]          grouped row carrying (t,k): group_offsets[g] + number
@@ -122,6 +147,9 @@ typedef struct ep_layout {
   int32_t* row_topk_idx;
   float* row_topk_weights;
   int64_t row_capacity;
+  int32_t* expert_row_src;
+  int64_t expert_row_capacity;
+  uint32_t* recv_stats;
 } ep_layout_t;
 
 /* Bytes of one packed fp8 row: H bytes of E4M3FN payload, then H/128
@@ -147,7 +175,8 @@ int ep_layout(const ep_problem_t* p, const int64_t* topk_idx, const float* topk_
               hipStream_t stream);
 
 /* Dispatch: scatter every token row of x (bf16 [T*H]) to the receive rows
- * the layout assigned it.
+ * the layout assigned it (with EP_FLAG_ZERO_PADDING also zero the expert
+ * alignment padding rows).
  *   rows == EP_ROWS_EXPERT: recv row slot[t,k] for each valid (t,k);
  *   rows == EP_ROWS_GROUP:  recv row grow[t,k] once per distinct row.
  *   format == EP_FORMAT_BF16: a receive row is the token's H bf16 values
@@ -178,17 +207,22 @@ int ep_dispatch(const ep_problem_t* p, const ep_layout_t* L, const void* x, void
  * valid selections of topk_weights[t,k] * y[slot[t,k]], with y bf16
  * [y_rows * H] in expert-major receive order (y row r is the expert output
  * for receive row r).  Each product and each sum is one fp32 rounding (no
- * fused multiply-add); accumulation starts from +0.
+ * fused multiply-add).
  *   order == EP_COMBINE_FLAT:    ascending k;
  *   order == EP_COMBINE_GROUPED: per group in ascending k, then the group
  *     partials in ascending group order (needs num_groups >= 1 and
  *     topk_idx int64 [T*K]; topk_idx may be NULL for the flat order).
- * A token with no valid selection gives +0 everywhere.  A slot >= y_rows
- * is skipped and sets status word EP_STATUS_COMBINE_OOB.  Every one of the
- * T output rows is written. */
+ * The accumulator starts at +0, or at the bias: bias0 and bias1 (bf16
+ * [T*H], either may be NULL) seed it as fl32(bias0 + bias1) (or the one
+ * given) instead of being added afterwards, so a token with no valid
+ * selection returns its bias, and +0 without one (the PR's combine bias,
+ * commit adding receive stats and combine bias).  In the grouped order the
+ * bias seeds the cross-group total.  A slot >= y_rows is skipped and sets
+ * status word EP_STATUS_COMBINE_OOB.  Every one of the T output rows is
+ * written. */
 int ep_combine(const ep_problem_t* p, const ep_layout_t* L, const int64_t* topk_idx,
-               const float* topk_weights, const void* y, int64_t y_rows, void* out,
-               int32_t order, hipStream_t stream);
+               const float* topk_weights, const void* y, int64_t y_rows, const void* bias0,
+               const void* bias1, void* out, int32_t order, hipStream_t stream);
 
 /* Static description of a return code. */
 const char* ep_strerror(int code);

@@ -45,6 +45,7 @@ def test_host_only_entry_points():
     assert ep.ep_layout_workspace_bytes(10, 8, 256, 7) == 0  # G must divide E
     assert ep.ep_layout_workspace_bytes(10, 33, 256) == 0  # K above the limit
     assert ep.ep_layout_workspace_bytes(10, 8, 1024, 8) == 0  # E + G above the limit
+    assert ep.fp8_row_pitch(7168) == 7424 and ep.fp8_row_pitch(128) == 256
     for c in range(5):
         assert ep.ep_strerror(c)
 
@@ -54,17 +55,20 @@ def test_invalid_arguments_return_codes_before_any_launch():
     from combine_ep_layout_03_amd import _lib
 
     L = _lib.lib()
-    p = _lib.Problem(16, 256, 8, 256, 0)
+    p = _lib.Problem(16, 256, 8, 256, 0, 0, 0)
     lay = _lib.LayoutStruct()
     # null layout outputs
     assert L.ep_layout(ctypes.byref(p), None, None, ctypes.byref(lay), None, 0, None) == _lib.EP_EINVAL
     # bad shapes
-    bad = _lib.Problem(16, 256, 0, 256, 0)
+    bad = _lib.Problem(16, 256, 0, 256, 0, 0, 0)
     assert L.ep_dispatch(ctypes.byref(bad), ctypes.byref(lay), None, None, 0, 0, 0, 0, None) == _lib.EP_EINVAL
-    bad = _lib.Problem(16, 256, 8, 256, 3)
-    assert L.ep_combine(ctypes.byref(bad), ctypes.byref(lay), None, None, None, 0, None, 0, None) == _lib.EP_EINVAL
+    bad = _lib.Problem(16, 256, 8, 256, 3, 0, 0)
+    assert L.ep_combine(ctypes.byref(bad), ctypes.byref(lay), None, None, None, 0, None, None, None, 0, None) == _lib.EP_EINVAL
+    # unknown flags and negative alignment are rejected
+    assert L.ep_dispatch(ctypes.byref(_lib.Problem(16, 256, 8, 256, 0, 0, 4)), ctypes.byref(lay), None, None, 0, 0, 0, 0, None) == _lib.EP_EINVAL
+    assert L.ep_dispatch(ctypes.byref(_lib.Problem(16, 256, 8, 256, 0, -1, 0)), ctypes.byref(lay), None, None, 0, 0, 0, 0, None) == _lib.EP_EINVAL
     # fp8 with hidden % 128 != 0 is unsupported (checked before pointers)
-    p2 = _lib.Problem(16, 100, 8, 256, 0)
+    p2 = _lib.Problem(16, 100, 8, 256, 0, 0, 0)
     lay.status = 8  # any non-null value; never dereferenced on this path
     assert (
         L.ep_dispatch(ctypes.byref(p2), ctypes.byref(lay), None, None, 0, 0, _lib.EP_ROWS_EXPERT, _lib.EP_FORMAT_FP8_PACKED, None)
@@ -76,15 +80,15 @@ def test_invalid_arguments_return_codes_before_any_launch():
         == _lib.EP_EINVAL
     )
     # T = 0 dispatch / combine are valid no-ops that launch nothing
-    p0 = _lib.Problem(0, 256, 8, 256, 0)
+    p0 = _lib.Problem(0, 256, 8, 256, 0, 0, 0)
     assert L.ep_dispatch(ctypes.byref(p0), ctypes.byref(lay), None, None, 0, 0, 0, 0, None) == _lib.EP_OK
     # a stride below the row size is rejected
-    p3 = _lib.Problem(16, 256, 8, 256, 0)
+    p3 = _lib.Problem(16, 256, 8, 256, 0, 0, 0)
     assert L.ep_dispatch(ctypes.byref(p3), ctypes.byref(lay), None, None, 0, 256, 0, 0, None) == _lib.EP_EINVAL
     # fp8 beyond the hidden limit
-    p4 = _lib.Problem(16, 32768 + 128, 8, 256, 0)
+    p4 = _lib.Problem(16, 32768 + 128, 8, 256, 0, 0, 0)
     assert L.ep_dispatch(ctypes.byref(p4), ctypes.byref(lay), None, None, 0, 0, 0, 1, None) == _lib.EP_ENOTSUP
-    assert L.ep_combine(ctypes.byref(p0), ctypes.byref(lay), None, None, None, 0, None, 0, None) == _lib.EP_OK
+    assert L.ep_combine(ctypes.byref(p0), ctypes.byref(lay), None, None, None, 0, None, None, None, 0, None) == _lib.EP_OK
 
 
 def test_binding_rejects_host_tensors():

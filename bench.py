@@ -57,6 +57,79 @@ def counted_traffic(op, workload):
     return rec.get("bytes_per_launch")
 
 
+def time_extras(ep, W, w, d_idx, d_wt, x, y, L, n_sel, rb, pitch, reps):
+    """Each op beside the headline step, timed alone (back to back, HIP
+    events on the current stream) at the same 8192 x 7168 workload:
+    grouped-order combine over 8 groups of 32 experts, the grouped (deduped)
+    fp8 dispatch, dispatch into 128-row-aligned expert segments with zeroed
+    padding, combine seeded by two bias rows, and the layout with
+    receive-stats accumulation."""
+    import torch
+
+    dev = x.device
+    T, H, K, E = w.T, w.H, w.K, w.E
+    stream = torch.cuda.current_stream(dev)
+    G = 8
+    LG = ep.ep_layout(d_idx, E, G, d_wt)
+    R = LG.num_rows(ep.EP_ROWS_GROUP)
+    LA = ep.ep_layout(d_idx, E, expert_alignment=128)
+    n_al = LA.num_rows()
+    out = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    recv_g = torch.empty(max(R, 1), pitch, dtype=torch.uint8, device=dev)
+    recv_a = torch.empty(LA.max_expert_rows(), pitch, dtype=torch.uint8, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(77)
+    b0 = torch.randn(T, H, generator=g, device=dev).to(torch.bfloat16)
+    b1 = torch.randn(T, H, generator=g, device=dev).to(torch.bfloat16)
+    stats = torch.zeros(E, dtype=torch.int32, device=dev)
+    comb_b = n_sel * H * 2 + T * K * 8 + T * H * 2
+    cases = {
+        "combine_grouped_g8": (
+            lambda: ep.ep_combine(y, LG, d_wt, d_idx, order=ep.EP_COMBINE_GROUPED, out=out),
+            comb_b + T * K * 8,
+        ),
+        "dispatch_fp8_grouped_rows_g8": (
+            lambda: ep.ep_dispatch(x, LG, fp8=True, rows=ep.EP_ROWS_GROUP, out=recv_g, capacity=R),
+            T * H * 2 + T * K * 4 + R * rb,
+        ),
+        "dispatch_fp8_align128_zero_padding": (
+            lambda: ep.ep_dispatch(x, LA, fp8=True, out=recv_a, zero_padding=True),
+            T * H * 2 + T * K * 4 + n_al * rb,
+        ),
+        "combine_bias2": (
+            lambda: ep.ep_combine(y, L, d_wt, out=out, bias0=b0, bias1=b1),
+            comb_b + 2 * T * H * 2,
+        ),
+        "layout_recv_stats": (
+            lambda: ep.ep_layout(d_idx, E, out=L, recv_stats=stats),
+            T * K * 12 + (2 * E + 1) * 4 + 2 * E * 4,
+        ),
+    }
+    res = {}
+    for name, (fn, nbytes) in cases.items():
+        fn()
+        a0 = torch.cuda.Event(enable_timing=True)
+        a1 = torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        for _ in range(reps):
+            fn()
+        a1.record(stream)
+        torch.cuda.synchronize()
+        us = a0.elapsed_time(a1) * 1e3 / reps
+        res[name] = {
+            "us": round(us, 2),
+            "bytes": int(nbytes),
+            "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "pct_of_peak": round(100.0 * nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
+        }
+    res["_note"] = (
+        f"grouped rows R={R} ({R / T:.3f} per token); aligned expert rows {n_al} "
+        f"(of which {n_al - n_sel} padding, counted as written bytes)"
+    )
+    ep.ep_layout(d_idx, E, out=L)  # restore the headline layout
+    return res
+
+
 def cpu_baseline(w, idx, wt, x_host, y_host, sample_tokens):
     """The CPU oracle, as it stands, timed on a bounded sample of the workload:
     the full layout, then fp8 dispatch and combine of the first
@@ -110,6 +183,11 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
     ap.add_argument("--bf16-dispatch", action="store_true", help="also time the bf16 dispatch variant")
+    ap.add_argument(
+        "--no-extras",
+        action="store_true",
+        help="skip the extra per-op timings (grouped combine, aligned dispatch, bias, stats)",
+    )
     ap.add_argument(
         "--isolated",
         action="store_true",
@@ -250,6 +328,7 @@ def main(argv=None):
             us = a0.elapsed_time(a1) * 1e3 / args.steps
             ops[name]["isolated_us"] = round(us, 2)
             ops[name]["isolated_GBps"] = round(ops[name]["bytes"] / (us * 1e-6) / 1e9, 1)
+    extras = {} if args.no_extras else time_extras(ep, W, w, d_idx, d_wt, x, y, L, n_sel, rb, pitch, args.steps)
     step_bytes = nb["layout"] + nb["dispatch_fp8"] + nb["combine"]
     step_ms = statistics.median(t_step)
     value = step_bytes / (step_ms * 1e-3) / 1e9
@@ -281,6 +360,7 @@ def main(argv=None):
             "parallelism": "single-GPU",
         },
         "ops": ops,
+        "extras": extras,
         "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
         "roofline": {
             "bound": "hbm",

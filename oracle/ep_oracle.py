@@ -55,6 +55,8 @@ __all__ = [
     "dispatch_fp8",
     "combine",
     "combine_grouped",
+    "expert_gemm",
+    "expert_gemm_bound",
 ]
 
 FP8_GROUP = 128  # elements per fp32 scale
@@ -409,3 +411,48 @@ def combine_grouped(
             P[sel] = (P[sel] + p).astype(np.float32)
         tot = (tot + P).astype(np.float32)
     return bf16_rne(tot)
+
+
+# --------------------------------------------------------------------------
+# grouped GEMM over the expert-major segments (the dispatch's consumer)
+# --------------------------------------------------------------------------
+def expert_gemm(x_u16, counts, offsets, w_u16, rows=None) -> np.ndarray:
+    """float64 y[r] = x[r] @ w[e]^T for every row r of expert e's segment
+    [offsets[e], offsets[e] + counts[e]); other rows are NaN (not defined).
+
+    ``w`` is bf16 [E, N, H] (expert e's N output rows, each H long).  The
+    products of bf16 values are exact in float64 and the sum is float64, so
+    this is the exact value to about 2^-50 relative; the GPU's fp32 sum and
+    bf16 output are compared against it within ``expert_gemm_bound``.  With
+    ``rows`` only those receive rows are computed (others NaN).  Used as the
+    grouped GEMM that consumes each expert's contiguous block of rows
+    (the mKernel article's MoE dispatch + grouped GEMM, consumer half).
+    """
+    x = bf16_to_f32(np.asarray(x_u16, dtype=np.uint16)).astype(np.float64)
+    w = bf16_to_f32(np.asarray(w_u16, dtype=np.uint16)).astype(np.float64)
+    E, N, H = w.shape
+    y = np.full((x.shape[0], N), np.nan)
+    want = None if rows is None else set(int(r) for r in rows)
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e]) + int(counts[e])
+        rs = [r for r in range(r0, r1) if want is None or r in want]
+        if rs:
+            y[rs] = x[rs] @ w[e].T
+    return y
+
+
+def expert_gemm_bound(x_u16, counts, offsets, w_u16, y64) -> np.ndarray:
+    """Per-element error bound for a bf16 result of an fp32-accumulated
+    expert GEMM: 2^-8 |y| (bf16 output rounding, with slack) plus
+    H * 2^-24 * sum_h |x w| (any order of H fp32 additions of exact
+    products).  NaN where y64 is NaN."""
+    x = np.abs(bf16_to_f32(np.asarray(x_u16, dtype=np.uint16)).astype(np.float64))
+    w = np.abs(bf16_to_f32(np.asarray(w_u16, dtype=np.uint16)).astype(np.float64))
+    E, N, H = w.shape
+    absdot = np.full_like(y64, np.nan)
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e]) + int(counts[e])
+        rs = [r for r in range(r0, r1) if not np.isnan(y64[r]).all()]
+        if rs:
+            absdot[rs] = x[rs] @ w[e].T
+    return np.abs(y64) * 2.0**-8 + absdot * H * 2.0**-24

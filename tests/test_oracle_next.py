@@ -109,3 +109,36 @@ def test_bias_masked_token_returns_bias_and_zero_bias_is_no_bias():
     g1 = O.combine_grouped(y, idx, slot, w, 12, 3, bias0=b0)
     assert np.array_equal(g1[2], b0[2])
     assert np.array_equal(O.combine_grouped(y, idx, slot, w, 12, 1, bias0=b0, bias1=b1), out2)
+
+
+def test_expert_gemm_bruteforce_and_segments():
+    rng = np.random.default_rng(12)
+    E, N, H = 3, 5, 7
+    counts = np.array([2, 0, 3])
+    offsets = np.array([0, 4, 4, 8])  # aligned to 4: rows 2,3 and 7 are padding
+    x = O.bf16_rne(rng.standard_normal((8, H)).astype(np.float32))
+    w = O.bf16_rne(rng.standard_normal((E, N, H)).astype(np.float32))
+    y = O.expert_gemm(x, counts, offsets, w)
+    xf, wf = O.bf16_to_f32(x).astype(np.float64), O.bf16_to_f32(w).astype(np.float64)
+    for r in range(8):
+        e = 0 if r < 2 else (2 if 4 <= r < 7 else None)
+        for n in range(N):
+            if e is None:
+                assert np.isnan(y[r, n])
+            else:
+                ref = sum(xf[r, h] * wf[e, n, h] for h in range(H))
+                assert abs(y[r, n] - ref) <= 1e-12 * max(1.0, abs(ref))
+    sub = O.expert_gemm(x, counts, offsets, w, rows=[1, 5])
+    assert np.array_equal(sub[[1, 5]], y[[1, 5]]) and np.isnan(sub[[0, 4, 6]]).all()
+    b = O.expert_gemm_bound(x, counts, offsets, w, y)
+    assert np.all(b[[0, 1, 4, 5, 6]] > 0)
+    # an fp32 sum in k order, rounded to bf16, sits inside the bound
+    got = np.full(8, np.nan)
+    for e in range(E):
+        for r in range(offsets[e], offsets[e] + counts[e]):
+            acc = np.float32(0.0)
+            for h in range(H):
+                acc = np.float32(acc + np.float32(xf[r, h] * wf[e, 0, h]))
+            got[r] = O.bf16_to_f32(O.bf16_rne(np.array([acc], np.float32)))[0]
+    ok = ~np.isnan(y[:, 0])
+    assert np.all(np.abs(got[ok] - y[ok, 0]) <= b[ok, 0])

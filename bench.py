@@ -122,6 +122,34 @@ def time_extras(ep, W, w, d_idx, d_wt, x, y, L, n_sel, rb, pitch, reps):
             "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
             "pct_of_peak": round(100.0 * nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
         }
+    # grouped GEMM consumer: receive rows @ per-expert weights, H -> 2048
+    N = 2048
+    xr = W.make_rows(w, L.max_expert_rows(), device=dev)
+    wts = W.make_expert_weights(w, N, device=dev)
+    yg = torch.empty(xr.shape[0], N, dtype=torch.bfloat16, device=dev)
+    fn = lambda: ep.ep_expert_gemm(xr, L, wts, out=yg)  # noqa: E731
+    fn()
+    a0 = torch.cuda.Event(enable_timing=True)
+    a1 = torch.cuda.Event(enable_timing=True)
+    gemm_reps = max(3, reps // 5)
+    a0.record(stream)
+    for _ in range(gemm_reps):
+        fn()
+    a1.record(stream)
+    torch.cuda.synchronize()
+    us = a0.elapsed_time(a1) * 1e3 / gemm_reps
+    flops = 2.0 * n_sel * H * N
+    nbytes = E * N * H * 2 + n_sel * H * 2 + n_sel * N * 2
+    res["expert_gemm_bf16_n2048"] = {
+        "us": round(us, 1),
+        "TFLOPs": round(flops / (us * 1e-6) / 1e12, 1),
+        "pct_of_mfma_peak": round(100.0 * flops / (us * 1e-6) / 2.5e15, 1),
+        "bytes": int(nbytes),
+        "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+        "pct_of_hbm_peak": round(100.0 * nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
+        "bound_us": {"mfma": round(flops / 2.5e15 * 1e6, 1), "hbm": round(nbytes / 8e12 * 1e6, 1)},
+    }
+    del xr, wts, yg
     res["_note"] = (
         f"grouped rows R={R} ({R / T:.3f} per token); aligned expert rows {n_al} "
         f"(of which {n_al - n_sel} padding, counted as written bytes)"

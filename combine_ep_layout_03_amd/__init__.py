@@ -43,6 +43,7 @@ __all__ = [
     "ep_layout",
     "ep_dispatch",
     "ep_combine",
+    "ep_expert_gemm",
     "ep_strerror",
     "EPError",
 ]
@@ -396,4 +397,42 @@ def ep_combine(
         _stream(y.device),
     )
     _lib.check("ep_combine", rc)
+    return out
+
+
+def ep_expert_gemm(
+    x: torch.Tensor,
+    layout: Layout,
+    w: torch.Tensor,
+    out: torch.Tensor | None = None,
+) -> torch.Tensor:
+    """Grouped GEMM over the expert-major segments: y[r] = x[r] @ w[e]^T for
+    each receive row r of expert e.  x: bf16 [rows, >= H] (row pitch = its
+    row size); w: bf16 [E, N, H]; returns y bf16 [rows, N] (rows outside the
+    experts' selections are left as they were)."""
+    layout = _resolve(layout)
+    if x.dim() != 2 or w.dim() != 3:
+        raise ValueError("x must be [rows, H] and w [E, N, H]")
+    _dev(x, "x", torch.bfloat16)
+    E, N, H = w.shape
+    if E != layout.num_experts:
+        raise ValueError("w must hold one [N, H] matrix per expert")
+    _dev(w, "w", torch.bfloat16)
+    if x.shape[1] < H:
+        raise ValueError("x rows are shorter than H")
+    if out is None:
+        out = torch.empty(x.shape[0], N, dtype=torch.bfloat16, device=x.device)
+    else:
+        _dev(out, "out", torch.bfloat16)
+        if out.dim() != 2 or out.shape[1] < N or out.shape[0] < x.shape[0]:
+            raise ValueError("out must be bf16 [>= rows, >= N]")
+    if x.shape[0] < layout.max_expert_rows():
+        raise ValueError("x must hold the layout's worst-case expert rows")
+    p = _problem(layout.num_tokens, H, layout.topk, layout.num_experts, layout.num_groups, layout.expert_alignment)
+    s = layout.struct()
+    rc = _lib.lib().ep_expert_gemm(
+        ctypes.byref(p), ctypes.byref(s), _ptr(x), int(x.shape[1]), _ptr(w), int(N), _ptr(out), int(out.shape[1]),
+        _stream(x.device),
+    )
+    _lib.check("ep_expert_gemm", rc)
     return out

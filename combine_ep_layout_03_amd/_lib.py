@@ -45,6 +45,7 @@ EXPORTS = (
     "ep_layout",
     "ep_dispatch",
     "ep_combine",
+    "ep_expert_gemm",
     "ep_strerror",
 )
 
@@ -113,6 +114,8 @@ def lib(path: str | None = None) -> ctypes.CDLL:
     L.ep_dispatch.restype = ctypes.c_int
     L.ep_combine.argtypes = [P, LS, vp, vp, vp, ctypes.c_int64, vp, vp, vp, ctypes.c_int32, vp]
     L.ep_combine.restype = ctypes.c_int
+    L.ep_expert_gemm.argtypes = [P, LS, vp, ctypes.c_int64, vp, ctypes.c_int32, vp, ctypes.c_int64, vp]
+    L.ep_expert_gemm.restype = ctypes.c_int
     L.ep_strerror.argtypes = [ctypes.c_int]
     L.ep_strerror.restype = ctypes.c_char_p
     if path is None:

@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libep_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
-SOURCES = ["ep_api.hip", "ep_layout.hip", "ep_dispatch.hip", "ep_combine.hip"]
+SOURCES = ["ep_api.hip", "ep_layout.hip", "ep_dispatch.hip", "ep_combine.hip", "ep_gemm.hip"]
 
 # test-only library exposing the device E4M3FN encoders (tests/hip)
 TEST_SOURCE = os.path.join(ROOT, "tests", "hip", "e4m3_check.hip")

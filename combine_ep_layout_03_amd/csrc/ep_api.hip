@@ -190,6 +190,37 @@ int ep_combine(const ep_problem_t* p, const ep_layout_t* L, const int64_t* topk_
   return ep::launch_combine(a, ve, stream) == hipSuccess ? EP_OK : EP_EHIP;
 }
 
+int ep_expert_gemm(const ep_problem_t* p, const ep_layout_t* L, const void* x,
+                   int64_t x_row_stride, const void* w, int32_t n_out, void* y,
+                   int64_t y_row_stride, hipStream_t stream) {
+  int rc = check_problem(p);
+  if (rc != EP_OK) return rc;
+  if (!L || !L->counts || !L->offsets || x_row_stride < 0 || y_row_stride < 0 || n_out < 1)
+    return EP_EINVAL;
+  if (p->hidden % 64 != 0 || n_out % 128 != 0) return EP_ENOTSUP;
+  const int64_t ldx = x_row_stride == 0 ? p->hidden : x_row_stride;
+  const int64_t ldy = y_row_stride == 0 ? n_out : y_row_stride;
+  if (ldx < p->hidden || ldy < n_out || ldx % 8 != 0 || ldy % 4 != 0) return EP_EINVAL;
+  if (p->num_tokens == 0) return EP_OK;
+  if (!x || !w || !y || !aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16)) return EP_EINVAL;
+  ep::GemmArgs a;
+  a.x = static_cast<const uint16_t*>(x);
+  a.ldx = ldx;
+  a.w = static_cast<const uint16_t*>(w);
+  a.y = static_cast<uint16_t*>(y);
+  a.ldy = ldy;
+  a.counts = L->counts;
+  a.offsets = L->offsets;
+  a.E = p->num_experts;
+  a.H = p->hidden;
+  a.N = n_out;
+  a.ntn = n_out / 128;
+  const int64_t pad = static_cast<int64_t>(p->num_experts) *
+                      (p->expert_alignment > 1 ? p->expert_alignment - 1 : 0);
+  const int64_t max_rows = p->num_tokens * p->topk + pad;
+  return ep::launch_expert_gemm(a, max_rows, stream) == hipSuccess ? EP_OK : EP_EHIP;
+}
+
 const char* ep_strerror(int code) {
   switch (code) {
     case EP_OK: return "ok";

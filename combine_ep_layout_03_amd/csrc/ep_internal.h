@@ -88,4 +88,19 @@ struct CombineArgs {
 // `vec_elems` in {8, 4, 2, 1} divides H and both base alignments (in bf16 elements).
 hipError_t launch_combine(const CombineArgs& a, int vec_elems, hipStream_t s);
 
+struct GemmArgs {
+  const uint16_t* x;  // bf16 receive rows, row stride ldx elements
+  int64_t ldx;
+  const uint16_t* w;  // bf16 [E, N, H]
+  uint16_t* y;        // bf16 output rows, row stride ldy elements
+  int64_t ldy;
+  const int32_t* counts;
+  const int32_t* offsets;
+  int E, H, N;
+  int ntn;  // N / 128
+};
+// H % 64 == 0, N % 128 == 0, E <= 1024, 16-byte aligned x / w / y and strides
+// (ldx % 8 == 0, ldy % 4 == 0); max_rows bounds the expert-major rows.
+hipError_t launch_expert_gemm(const GemmArgs& a, int64_t max_rows, hipStream_t s);
+
 }  // namespace ep

@@ -32,47 +32,6 @@ __device__ __forceinline__ bool first_in_group(const int64_t* __restrict__ idx, 
   return true;
 }
 
-// Exclusive scan of a[0..n) in LDS, n <= 4 * kBlock.  Returns the total.
-// Every thread of the block must call it.
-__device__ int block_exclusive_scan(int* a, int n, int* tmp) {
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
-  const int i0 = tid * 4;
-  int v[4];
-  int s = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    v[j] = (i0 + j < n) ? a[i0 + j] : 0;
-    s += v[j];
-  }
-  int x = s;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int y = __shfl_up(x, off, kWave);
-    if (lane >= off) x += y;
-  }
-  if (lane == kWave - 1) tmp[wave] = x;
-  __syncthreads();
-  int before = 0, total = 0;
-#pragma unroll
-  for (int w = 0; w < kWavesPerBlock; ++w) {
-    const int t = tmp[w];
-    if (w < wave) before += t;
-    total += t;
-  }
-  int run = before + x - s;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if (i0 + j < n) {
-      a[i0 + j] = run;
-      run += v[j];
-    }
-  }
-  __syncthreads();
-  return total;
-}
-
 template <bool GROUPED>
 __global__ __launch_bounds__(kBlock) void k_layout_count(const int64_t* __restrict__ idx,
                                                          uint32_t n, int K, int E, int epg,

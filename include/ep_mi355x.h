@@ -224,6 +224,25 @@ int ep_combine(const ep_problem_t* p, const ep_layout_t* L, const int64_t* topk_
                const float* topk_weights, const void* y, int64_t y_rows, const void* bias0,
                const void* bias1, void* out, int32_t order, hipStream_t stream);
 
+/* Grouped GEMM over the expert-major segments (the consumer of dispatch;
+ * the mKernel article's MoE dispatch + grouped GEMM, one-GPU consumer
+ * half): for every expert e and receive row r in [offsets[e],
+ * offsets[e] + counts[e]),
+ *   y[r, n] = bf16_rne( sum over h < H of x[r, h] * w[e, n, h] ),  n < n_out,
+ * summed in fp32 in the matrix cores' order (so results agree with an exact
+ * sum within 2^-8 |y| + H 2^-24 sum |x w|, not bit for bit).
+ *   x  bf16 receive rows (ep_dispatch's bf16 output), row r at element
+ *      r * x_row_stride (0 = H);
+ *   w  bf16 [E, n_out, H]: expert e's n_out output rows, each H long;
+ *   y  bf16 output rows, row r at element r * y_row_stride (0 = n_out).
+ * Rows outside every expert's selections (alignment padding, rows past the
+ * layout) are not written.  Requires H % 64 == 0 and n_out % 128 == 0
+ * (EP_ENOTSUP otherwise), 16-byte aligned x, w and y, x_row_stride a
+ * multiple of 8 and y_row_stride a multiple of 4. */
+int ep_expert_gemm(const ep_problem_t* p, const ep_layout_t* L, const void* x,
+                   int64_t x_row_stride, const void* w, int32_t n_out, void* y,
+                   int64_t y_row_stride, hipStream_t stream);
+
 /* Static description of a return code. */
 const char* ep_strerror(int code);
 

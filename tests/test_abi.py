@@ -18,7 +18,7 @@ def _declared():
 
 def test_header_declares_the_boundary():
     assert _declared() == sorted(
-        ["ep_fp8_row_bytes", "ep_layout_workspace_bytes", "ep_layout", "ep_dispatch", "ep_combine", "ep_strerror"]
+        ["ep_fp8_row_bytes", "ep_layout_workspace_bytes", "ep_layout", "ep_dispatch", "ep_combine", "ep_expert_gemm", "ep_strerror"]
     )
 
 

@@ -1,0 +1,116 @@
+"""GPU parity of the grouped GEMM over expert segments (MFMA, bf16 in, fp32
+accumulate, bf16 out) against the float64 oracle, within the bound derived
+from the arithmetic: |y - y64| <= 2^-8 |y64| + H 2^-24 sum |x w| per element,
+and rel_l2 <= 1e-2 overall."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import ep_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.synchronize()
+
+
+def ep():
+    import combine_ep_layout_03_amd as m
+
+    return m
+
+
+def u16(t):
+    return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def _check(got_u16, x_u16, counts, offsets, w_u16, rows=None):
+    y64 = O.expert_gemm(x_u16, counts, offsets, w_u16, rows=rows)
+    bound = O.expert_gemm_bound(x_u16, counts, offsets, w_u16, y64)
+    ok = ~np.isnan(y64)
+    got = O.bf16_to_f32(got_u16).astype(np.float64)
+    err = np.abs(got - y64)
+    bad = ok & ~(err <= bound)
+    assert not bad.any(), f"{bad.sum()} elements out of bound, worst {np.nanmax(err - bound)}"
+    rel = np.linalg.norm((got - y64)[ok]) / np.linalg.norm(y64[ok])
+    assert rel <= 1e-2, rel
+    return rel
+
+
+@pytest.mark.parametrize("T,K,E,H,N,A", [(300, 2, 8, 256, 256, 0), (257, 4, 16, 128, 128, 0), (700, 3, 12, 192, 384, 64)])
+def test_expert_gemm_small(T, K, E, H, N, A):
+    w = W.Workload("g", T=T, H=H, K=K, E=E, mask_p=0.1, seed=T)
+    idx, _ = W.make_routing(w)
+    R = O.layout(idx.numpy(), E, expert_alignment=A)
+    L = ep().ep_layout(idx.to(DEV), E, expert_alignment=A)
+    rows = L.max_expert_rows()
+    x = W.make_rows(w, rows)
+    wts = W.make_expert_weights(w, N)
+    y = torch.full((rows, N), -1, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    ep().ep_expert_gemm(x.to(DEV), L, wts.to(DEV), out=y)
+    got = u16(y)
+    _check(got, u16(x), R["counts"], R["offsets"], u16(wts))
+    # rows outside every expert's selections stay untouched
+    occupied = np.zeros(rows, bool)
+    for e in range(E):
+        occupied[R["offsets"][e] : R["offsets"][e] + R["counts"][e]] = True
+    assert (got[~occupied] == 0xFFFF).all()
+
+
+def test_expert_gemm_skewed_with_empty_experts():
+    w = W.by_name("skewed_masked").replace(T=2000, H=256, E=64)
+    idx, _ = W.make_routing(w)
+    R = O.layout(idx.numpy(), w.E, expert_alignment=16)
+    assert (R["counts"] == 0).any() or R["counts"].max() > 3 * 128
+    L = ep().ep_layout(idx.to(DEV), w.E, expert_alignment=16)
+    x = W.make_rows(w, L.max_expert_rows())
+    wts = W.make_expert_weights(w, 256)
+    y = ep().ep_expert_gemm(x.to(DEV), L, wts.to(DEV))
+    _check(u16(y), u16(x), R["counts"], R["offsets"], u16(wts))
+
+
+def test_expert_gemm_pages_shape_sampled():
+    """8192 tokens x top-8 of 256 experts, H = 7168 -> N = 2048, on 64 sampled
+    rows from 8 experts (their first, last and random rows)."""
+    w = W.by_name("pages")
+    N = 2048
+    print("gemm pages shape: inputs", flush=True)
+    idx, _ = W.make_routing(w)
+    R = O.layout(idx.numpy(), w.E)
+    L = ep().ep_layout(idx.to(DEV), w.E)
+    x = W.make_rows(w, L.max_expert_rows(), device=DEV)
+    wts = W.make_expert_weights(w, N, device=DEV)
+    print("gemm pages shape: run", flush=True)
+    y = ep().ep_expert_gemm(x, L, wts)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    experts = rng.choice(w.E, 8, replace=False)
+    rows = []
+    for e in experts:
+        r0, c = int(R["offsets"][e]), int(R["counts"][e])
+        rows += [r0, r0 + c - 1] + list(rng.choice(np.arange(r0, r0 + c), 6, replace=False))
+    rows = np.array(sorted(set(rows)))
+    # the oracle sees only the sampled rows and their experts' weights
+    sub_counts = np.zeros(len(experts), np.int64)
+    sub_offsets = np.zeros(len(experts) + 1, np.int64)
+    order = []
+    for i, e in enumerate(sorted(experts)):
+        r0, c = int(R["offsets"][e]), int(R["counts"][e])
+        mine = [r for r in rows if r0 <= r < r0 + c]
+        order += mine
+        sub_counts[i] = len(mine)
+        sub_offsets[i + 1] = sub_offsets[i] + len(mine)
+    sel = torch.from_numpy(np.array(order)).to(DEV)
+    xs = u16(x.index_select(0, sel))
+    ws = u16(wts.index_select(0, torch.from_numpy(np.sort(experts)).to(DEV)))
+    ys = u16(y.index_select(0, sel))
+    rel = _check(ys, xs, sub_counts, sub_offsets, ws)
+    print("rel_l2", rel, flush=True)

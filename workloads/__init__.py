@@ -39,10 +39,12 @@ __all__ = [
     "make_routing",
     "make_y",
     "tiny_expert_outputs",
+    "make_expert_weights",
+    "make_rows",
 ]
 
 # sub-stream ids
-_S_X, _S_ROUTE, _S_PERM, _S_MASK, _S_FULLMASK, _S_W, _S_Y = range(7)
+_S_X, _S_ROUTE, _S_PERM, _S_MASK, _S_FULLMASK, _S_W, _S_Y, _S_EW, _S_RX = range(9)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -168,3 +170,19 @@ def tiny_expert_outputs(recv: torch.Tensor, row_expert: torch.Tensor) -> torch.T
     f = 1.0 + row_expert.to(torch.float32) / 16.0
     return (recv.to(torch.float32) * f[:, None]).to(torch.bfloat16)
 
+
+
+def make_expert_weights(w: Workload, n_out: int, device="cpu") -> torch.Tensor:
+    """bf16 [E, n_out, H] random expert weights, N(0, 1/H), so a row of N(0,1)
+    inputs maps to outputs of unit scale (random init: no trained weights)."""
+    g = _gen(w, _S_EW, device)
+    out = torch.empty(w.E, n_out, w.H, dtype=torch.bfloat16, device=device)
+    for e in range(w.E):  # one expert at a time keeps the fp32 temporary small
+        out[e] = (torch.randn(n_out, w.H, generator=g, device=device) * w.H**-0.5).to(torch.bfloat16)
+    return out
+
+
+def make_rows(w: Workload, rows: int, device="cpu") -> torch.Tensor:
+    """bf16 [rows, H] N(0,1) receive rows for a consumer of the dispatch."""
+    g = _gen(w, _S_RX, device)
+    return torch.randn(rows, w.H, generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)

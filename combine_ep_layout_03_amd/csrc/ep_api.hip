@@ -214,7 +214,7 @@ int ep_expert_gemm(const ep_problem_t* p, const ep_layout_t* L, const void* x,
   a.E = p->num_experts;
   a.H = p->hidden;
   a.N = n_out;
-  a.ntn = n_out / 128;
+  a.ntn = (n_out + 255) / 256;
   const int64_t pad = static_cast<int64_t>(p->num_experts) *
                       (p->expert_alignment > 1 ? p->expert_alignment - 1 : 0);
   const int64_t max_rows = p->num_tokens * p->topk + pad;

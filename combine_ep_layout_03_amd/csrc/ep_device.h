@@ -122,17 +122,21 @@ struct VecOf<2> {
   using type = uint16_t;
 };
 
-// Exclusive scan of a[0..n) in LDS, n <= 4 * kBlock.  Returns the total.
-// Every thread of the block must call it.
+// Exclusive scan of a[0..n) in LDS, n <= 1024, by a block of NT threads
+// (NT a multiple of 64 dividing 1024).  tmp holds NT / 64 ints.  Returns the
+// total.  Every thread of the block must call it: it contains barriers.
+template <int NT = kBlock>
 __device__ __forceinline__ int block_exclusive_scan(int* a, int n, int* tmp) {
+  constexpr int kItems = 1024 / NT;
+  constexpr int kWaves = NT / kWave;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
-  const int i0 = tid * 4;
-  int v[4];
+  const int i0 = tid * kItems;
+  int v[kItems];
   int s = 0;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < kItems; ++j) {
     v[j] = (i0 + j < n) ? a[i0 + j] : 0;
     s += v[j];
   }
@@ -146,14 +150,14 @@ __device__ __forceinline__ int block_exclusive_scan(int* a, int n, int* tmp) {
   __syncthreads();
   int before = 0, total = 0;
 #pragma unroll
-  for (int w = 0; w < kWavesPerBlock; ++w) {
+  for (int w = 0; w < kWaves; ++w) {
     const int t = tmp[w];
     if (w < wave) before += t;
     total += t;
   }
   int run = before + x - s;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < kItems; ++j) {
     if (i0 + j < n) {
       a[i0 + j] = run;
       run += v[j];

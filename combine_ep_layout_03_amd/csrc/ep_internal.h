@@ -97,7 +97,7 @@ struct GemmArgs {
   const int32_t* counts;
   const int32_t* offsets;
   int E, H, N;
-  int ntn;  // N / 128
+  int ntn;  // column tiles, ceil(N / 256)
 };
 // H % 64 == 0, N % 128 == 0, E <= 1024, 16-byte aligned x / w / y and strides
 // (ldx % 8 == 0, ldy % 4 == 0); max_rows bounds the expert-major rows.

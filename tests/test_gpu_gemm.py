@@ -45,7 +45,16 @@ def _check(got_u16, x_u16, counts, offsets, w_u16, rows=None):
     return rel
 
 
-@pytest.mark.parametrize("T,K,E,H,N,A", [(300, 2, 8, 256, 256, 0), (257, 4, 16, 128, 128, 0), (700, 3, 12, 192, 384, 64)])
+@pytest.mark.parametrize(
+    "T,K,E,H,N,A",
+    [
+        (300, 2, 8, 256, 256, 0),
+        (257, 4, 16, 128, 128, 0),
+        (700, 3, 12, 192, 384, 64),
+        (90, 2, 4, 64, 128, 0),  # two reduction steps: fewer than the ring's depth
+        (1500, 2, 4, 320, 256, 0),  # ~750 rows per expert: three row tiles each
+    ],
+)
 def test_expert_gemm_small(T, K, E, H, N, A):
     w = W.Workload("g", T=T, H=H, K=K, E=E, mask_p=0.1, seed=T)
     idx, _ = W.make_routing(w)
@@ -63,6 +72,25 @@ def test_expert_gemm_small(T, K, E, H, N, A):
     for e in range(E):
         occupied[R["offsets"][e] : R["offsets"][e] + R["counts"][e]] = True
     assert (got[~occupied] == 0xFFFF).all()
+
+
+def test_expert_gemm_exact_on_small_integers():
+    """Integer inputs in [-2, 2] make every fp32 partial sum exact, so the
+    kernel's output must equal the bf16 rounding of the exact sum bit for bit:
+    any row, column or k misplacement shows as a mismatch."""
+    w = W.Workload("gi", T=1200, H=448, K=3, E=6, mask_p=0.05, seed=11)
+    N = 384
+    idx, _ = W.make_routing(w)
+    R = O.layout(idx.numpy(), w.E, expert_alignment=32)
+    L = ep().ep_layout(idx.to(DEV), w.E, expert_alignment=32)
+    rows = L.max_expert_rows()
+    x = W.make_small_ints(w, (rows, w.H), stream=0)
+    wts = W.make_small_ints(w, (w.E, N, w.H), stream=1)
+    y = ep().ep_expert_gemm(x.to(DEV), L, wts.to(DEV))
+    y64 = O.expert_gemm(u16(x), R["counts"], R["offsets"], u16(wts))
+    ok = ~np.isnan(y64)
+    want = O.bf16_rne(y64[ok].astype(np.float32))
+    assert np.array_equal(u16(y)[ok], want)
 
 
 def test_expert_gemm_skewed_with_empty_experts():

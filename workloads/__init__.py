@@ -44,7 +44,7 @@ __all__ = [
 ]
 
 # sub-stream ids
-_S_X, _S_ROUTE, _S_PERM, _S_MASK, _S_FULLMASK, _S_W, _S_Y, _S_EW, _S_RX = range(9)
+_S_X, _S_ROUTE, _S_PERM, _S_MASK, _S_FULLMASK, _S_W, _S_Y, _S_EW, _S_RX, _S_INT = range(10)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -186,3 +186,12 @@ def make_rows(w: Workload, rows: int, device="cpu") -> torch.Tensor:
     """bf16 [rows, H] N(0,1) receive rows for a consumer of the dispatch."""
     g = _gen(w, _S_RX, device)
     return torch.randn(rows, w.H, generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+
+
+def make_small_ints(w: Workload, shape, lo: int = -2, hi: int = 2, stream: int = 0,
+                    device="cpu") -> torch.Tensor:
+    """bf16 tensor of integers drawn uniformly from [lo, hi]: products and
+    sums of a few thousand of them are exact in fp32, so any summation order
+    gives the same value."""
+    g = _gen(w, _S_INT * 16 + stream, device)
+    return torch.randint(lo, hi + 1, tuple(shape), generator=g, device=device).to(torch.bfloat16)

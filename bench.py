@@ -57,13 +57,14 @@ def counted_traffic(op, workload):
     return rec.get("bytes_per_launch")
 
 
-def time_extras(ep, W, w, d_idx, d_wt, x, y, L, n_sel, rb, pitch, reps):
+def time_extras(ep, W, w, d_idx, d_wt, x, y, L, n_sel, rb, pitch, reps, only=None):
     """Each op beside the headline step, timed alone (back to back, HIP
     events on the current stream) at the same 8192 x 7168 workload:
     grouped-order combine over 8 groups of 32 experts, the grouped (deduped)
     fp8 dispatch, dispatch into 128-row-aligned expert segments with zeroed
     padding, combine seeded by two bias rows, and the layout with
-    receive-stats accumulation."""
+    receive-stats accumulation, and the grouped GEMM consumer.  ``only``, if
+    given, names the cases to run."""
     import torch
 
     dev = x.device
@@ -107,6 +108,8 @@ def time_extras(ep, W, w, d_idx, d_wt, x, y, L, n_sel, rb, pitch, reps):
     }
     res = {}
     for name, (fn, nbytes) in cases.items():
+        if only is not None and name not in only:
+            continue
         fn()
         a0 = torch.cuda.Event(enable_timing=True)
         a1 = torch.cuda.Event(enable_timing=True)
@@ -124,6 +127,9 @@ def time_extras(ep, W, w, d_idx, d_wt, x, y, L, n_sel, rb, pitch, reps):
         }
     # grouped GEMM consumer: receive rows @ per-expert weights, H -> 2048
     N = 2048
+    if only is not None and "expert_gemm_bf16_n2048" not in only:
+        ep.ep_layout(d_idx, E, out=L)
+        return res
     xr = W.make_rows(w, L.max_expert_rows(), device=dev)
     wts = W.make_expert_weights(w, N, device=dev)
     yg = torch.empty(xr.shape[0], N, dtype=torch.bfloat16, device=dev)
@@ -148,6 +154,7 @@ def time_extras(ep, W, w, d_idx, d_wt, x, y, L, n_sel, rb, pitch, reps):
         "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
         "pct_of_hbm_peak": round(100.0 * nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
         "bound_us": {"mfma": round(flops / 2.5e15 * 1e6, 1), "hbm": round(nbytes / 8e12 * 1e6, 1)},
+        "traffic": counted_traffic("expert_gemm_n2048", w.name),
     }
     del xr, wts, yg
     res["_note"] = (
@@ -202,6 +209,27 @@ def cpu_baseline(w, idx, wt, x_host, y_host, sample_tokens):
     }
 
 
+def smi_snapshot():
+    """GPU busy percentage of every amdgpu device and the processes holding a
+    GPU context, read from sysfs (the driver's gpu_busy_percent and the KFD
+    process list): the idle check, without starting any other program."""
+    import glob
+
+    out = {"busy_percent": {}, "kfd_processes": None}
+    for f in sorted(glob.glob("/sys/class/drm/card[0-9]*/device/gpu_busy_percent")):
+        try:
+            with open(f) as fh:
+                out["busy_percent"][f.split("/")[4]] = int(fh.read().strip())
+        except (OSError, ValueError):
+            pass
+    try:
+        pids = sorted(int(p) for p in os.listdir("/sys/class/kfd/kfd/proc") if p.isdigit())
+        out["kfd_processes"] = {"count": len(pids), "self_listed": os.getpid() in pids}
+    except OSError:
+        pass
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -220,6 +248,18 @@ def main(argv=None):
         "--isolated",
         action="store_true",
         help="also time each op alone, back to back, outside the step (diagnostic)",
+    )
+    ap.add_argument(
+        "--extras",
+        default=None,
+        metavar="NAMES",
+        help="comma-separated names of the extra timings to run (default: all)",
+    )
+    ap.add_argument(
+        "--no-cold",
+        action="store_true",
+        help="skip the cold-cache pass (a 1 GiB buffer is written before each step, so the "
+        "256 MB last-level cache cannot serve the step's inputs)",
     )
     ap.add_argument(
         "--calibrate-copy",
@@ -268,8 +308,9 @@ def main(argv=None):
 
     stream = torch.cuda.current_stream(dev)
     ev = {k: [] for k in ("start", "layout", "dispatch", "combine", "bf16")}
+    gpu_state = {"before": smi_snapshot()}
 
-    def step(record):
+    def step(record, ev=ev):
         if record:
             e0 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
@@ -305,9 +346,21 @@ def main(argv=None):
         step(True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    gpu_state["after"] = smi_snapshot()
 
-    def ms(a, b):
-        return [x.elapsed_time(y) for x, y in zip(ev[a], ev[b])]
+    ev_cold = {k: [] for k in ev}
+    if not args.no_cold:
+        # cold caches: write 1 GiB before every step (outside the timed events)
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        for i in range(args.steps):
+            scratch.fill_(i & 0xFF)
+            step(True, ev_cold)
+        torch.cuda.synchronize()
+        del scratch
+        print("# cold-cache pass done", file=sys.stderr, flush=True)
+
+    def ms(a, b, evd=ev):
+        return [x.elapsed_time(y) for x, y in zip(evd[a], evd[b])]
 
     t_layout = ms("start", "layout")
     t_disp = ms("layout", "dispatch")
@@ -330,9 +383,26 @@ def main(argv=None):
         "layout": stats(t_layout, nb["layout"]),
         "dispatch_fp8": stats(t_disp, nb["dispatch_fp8"]),
         "combine": stats(t_comb, nb["combine"]),
+        # dispatch as the pages time a collective: layout and scatter together
+        "dispatch_e2e": stats([a + b for a, b in zip(t_layout, t_disp)], nb["layout"] + nb["dispatch_fp8"]),
     }
     if t_bf16:
         ops["dispatch_bf16"] = stats(t_bf16, nb["dispatch_bf16"])
+    ops_cold = None
+    if ev_cold["start"]:
+        c_layout = ms("start", "layout", ev_cold)
+        c_disp = ms("layout", "dispatch", ev_cold)
+        c_comb = ms("dispatch", "combine", ev_cold)
+        ops_cold = {
+            "layout": stats(c_layout, nb["layout"]),
+            "dispatch_fp8": stats(c_disp, nb["dispatch_fp8"]),
+            "combine": stats(c_comb, nb["combine"]),
+            "dispatch_e2e": stats([a + b for a, b in zip(c_layout, c_disp)], nb["layout"] + nb["dispatch_fp8"]),
+            "step": stats([a + b + c for a, b, c in zip(c_layout, c_disp, c_comb)],
+                          nb["layout"] + nb["dispatch_fp8"] + nb["combine"]),
+        }
+        if recv16 is not None:
+            ops_cold["dispatch_bf16"] = stats(ms("combine", "bf16", ev_cold), nb["dispatch_bf16"])
     if args.isolated:
         iso = {
             "layout": lambda: ep.ep_layout(d_idx, E, out=L),
@@ -356,7 +426,8 @@ def main(argv=None):
             us = a0.elapsed_time(a1) * 1e3 / args.steps
             ops[name]["isolated_us"] = round(us, 2)
             ops[name]["isolated_GBps"] = round(ops[name]["bytes"] / (us * 1e-6) / 1e9, 1)
-    extras = {} if args.no_extras else time_extras(ep, W, w, d_idx, d_wt, x, y, L, n_sel, rb, pitch, args.steps)
+    only = None if args.extras is None else set(s for s in args.extras.split(",") if s)
+    extras = {} if args.no_extras else time_extras(ep, W, w, d_idx, d_wt, x, y, L, n_sel, rb, pitch, args.steps, only)
     step_bytes = nb["layout"] + nb["dispatch_fp8"] + nb["combine"]
     step_ms = statistics.median(t_step)
     value = step_bytes / (step_ms * 1e-3) / 1e9
@@ -388,7 +459,9 @@ def main(argv=None):
             "parallelism": "single-GPU",
         },
         "ops": ops,
+        "ops_cold_cache": ops_cold,
         "extras": extras,
+        "gpu_state": gpu_state,
         "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
         "roofline": {
             "bound": "hbm",

@@ -258,8 +258,8 @@ def main(argv=None):
     ap.add_argument(
         "--no-cold",
         action="store_true",
-        help="skip the cold-cache pass (a 1 GiB buffer is written before each step, so the "
-        "256 MB last-level cache cannot serve the step's inputs)",
+        help="skip the cold-cache pass (a 1 GiB buffer is read before each step, so the "
+        "256 MB memory-side cache cannot serve the step's inputs)",
     )
     ap.add_argument(
         "--calibrate-copy",
@@ -350,13 +350,17 @@ def main(argv=None):
 
     ev_cold = {k: [] for k in ev}
     if not args.no_cold:
-        # cold caches: write 1 GiB before every step (outside the timed events)
-        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        for i in range(args.steps):
-            scratch.fill_(i & 0xFF)
+        # cold caches: read 1 GiB before every step (outside the timed
+        # events), which evicts the step's inputs from L2 and the 256 MB
+        # memory-side cache without leaving dirty lines to write back during
+        # the step
+        scratch = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+        sink = torch.zeros((), dtype=torch.int64, device=dev)
+        for _ in range(args.steps):
+            sink += scratch.sum()
             step(True, ev_cold)
         torch.cuda.synchronize()
-        del scratch
+        del scratch, sink
         print("# cold-cache pass done", file=sys.stderr, flush=True)
 
     def ms(a, b, evd=ev):

@@ -90,78 +90,117 @@ __global__ __launch_bounds__(kBlock) void k_scatter_bf16(ScatterArgs a, int nchu
 // bytes: q[0..H) | s_0 .. s_{H/128-1} (fp32, little-endian) | zeros to row_bytes.
 // A wave owns whole tokens.  Each lane converts 16 consecutive elements per
 // step, so 8 lanes form one group and a step covers 1024 elements
-// (H % 128 == 0 keeps every group's 8 lanes together and active).  The
-// group scales stay in registers (group g in lane g % 64, slot g / 64) until
-// the payload is out, then each destination row gets its scales and padding
-// in one store: one sweep over the row per destination.  Writing the scales
-// piecewise per step, or at the packed 7392-byte pitch instead of a
-// 128-byte aligned one, measured 20-45% slower at hidden 7168.
-template <int KMAX>
+// (H % 128 == 0 keeps every group's 8 lanes together and active).  A step's
+// source elements are loaded one step ahead (the next token's first step
+// during the last step of a token), so the loads fly while a step converts.
+// The group scales stay in registers (group g in lane g % 64, slot g / 64).
+// With ROWBUF (H <= 8192) the token's whole payload stays in registers too,
+// and each destination row is then written in one burst: payload, scales,
+// padding.  Otherwise each step's payload is stored as it is made and the
+// scales follow the last step (the launcher picks by row pitch).  Writing the scales piecewise per step, or
+// at the packed 7392-byte pitch instead of a 128-byte aligned one, measured
+// 20-45% slower at hidden 7168.
+template <int KMAX, bool ROWBUF>
 __global__ __launch_bounds__(kBlock) void k_scatter_fp8(ScatterArgs a, int64_t row_bytes) {
   constexpr int kMaxScaleSlots = 4;  // H <= 4 * 64 * 128
+  constexpr int kRowSteps = 8;       // ROWBUF: H <= 8 * 1024
   if (static_cast<int64_t>(*a.rows_needed) > a.capacity) return;
   const int lane = threadIdx.x & (kWave - 1);
   int64_t t, t_end;
   wave_range(a.T, t, t_end);
+  if (t >= t_end) return;
   const int H = a.H;
   const int ngroups = H / 128;
   const int nsteps = (H + kWave * 16 - 1) / (kWave * 16);
   const int pad_words = static_cast<int>((row_bytes - H - 4 * ngroups) / 4);
+  const uint16_t* const x = static_cast<const uint16_t*>(a.x);
   char* rbase = static_cast<char*>(a.recv);
+  u32x4 nx0 = {0u, 0u, 0u, 0u}, nx1 = {0u, 0u, 0u, 0u};
+  auto load_step = [&](int64_t tt, int c) {
+    const int el = c * (kWave * 16) + lane * 16;
+    if (el < H) {
+      const uint16_t* src = x + tt * H + el;
+      nx0 = *reinterpret_cast<const u32x4*>(src);
+      nx1 = *reinterpret_cast<const u32x4*>(src + 8);
+    }
+  };
+  // convert step c of token t (inputs already in nx0/nx1), start the next
+  // load, and file the step's group scales; returns the step's 16 codes
+  float my_sc[kMaxScaleSlots];
+  auto convert_step = [&](int64_t tt, int c) -> u32x4 {
+    const int el = c * (kWave * 16) + lane * 16;
+    const bool act = el < H;
+    const u32x4 in0 = act ? nx0 : u32x4{0u, 0u, 0u, 0u};
+    const u32x4 in1 = act ? nx1 : u32x4{0u, 0u, 0u, 0u};
+    if (c + 1 < nsteps) load_step(tt, c + 1);
+    else if (tt + 1 < t_end) load_step(tt + 1, 0);
+    float f[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = bf16_lo(in0[i]);
+      f[2 * i + 1] = bf16_hi(in0[i]);
+      f[8 + 2 * i] = bf16_lo(in1[i]);
+      f[8 + 2 * i + 1] = bf16_hi(in1[i]);
+    }
+    float am = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(f[i]));
+    am = fmaxf(am, __shfl_xor(am, 1, kWave));
+    am = fmaxf(am, __shfl_xor(am, 2, kWave));
+    am = fmaxf(am, __shfl_xor(am, 4, kWave));
+    const float s = am / 448.0f;
+    u32x4 q = {0u, 0u, 0u, 0u};
+    if (s != 0.0f) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = e4m3fn_sat_pair(f[4 * i] / s, f[4 * i + 1] / s);
+        const uint32_t hi = e4m3fn_sat_pair(f[4 * i + 2] / s, f[4 * i + 3] / s);
+        q[i] = lo | (hi << 16);
+      }
+    }
+    // this step's groups are c*8 .. c*8+7; group c*8+g goes to lane
+    // (c*8+g) % 64, which is lane (c%8)*8 + g, register slot c/8
+    const float sc = __shfl(s, (lane & 7) * 8, kWave);
+    const bool keep = (lane >> 3) == (c & 7);
+#pragma unroll
+    for (int r = 0; r < kMaxScaleSlots; ++r)
+      if (keep && r == (c >> 3)) my_sc[r] = sc;
+    return q;
+  };
+  load_step(t, 0);
   for (; t < t_end; ++t) {
     int d[KMAX];
     load_dests<KMAX>(a, t, lane, d);
-    const uint16_t* xr = static_cast<const uint16_t*>(a.x) + t * H;
-    float my_sc[kMaxScaleSlots] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int c = 0; c < nsteps; ++c) {
-      const int el = c * (kWave * 16) + lane * 16;
-      const bool act = el < H;
-      u32x4 in0 = {0u, 0u, 0u, 0u}, in1 = {0u, 0u, 0u, 0u};
-      if (act) {
-        in0 = *reinterpret_cast<const u32x4*>(xr + el);
-        in1 = *reinterpret_cast<const u32x4*>(xr + el + 8);
-      }
-      float f[16];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f[2 * i] = bf16_lo(in0[i]);
-        f[2 * i + 1] = bf16_hi(in0[i]);
-        f[8 + 2 * i] = bf16_lo(in1[i]);
-        f[8 + 2 * i + 1] = bf16_hi(in1[i]);
-      }
-      float am = 0.0f;
+    for (int r = 0; r < kMaxScaleSlots; ++r) my_sc[r] = 0.0f;
+    u32x4 qrow[ROWBUF ? kRowSteps : 1];
+    if constexpr (ROWBUF) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(f[i]));
-      am = fmaxf(am, __shfl_xor(am, 1, kWave));
-      am = fmaxf(am, __shfl_xor(am, 2, kWave));
-      am = fmaxf(am, __shfl_xor(am, 4, kWave));
-      const float s = am / 448.0f;
-      u32x4 q = {0u, 0u, 0u, 0u};
-      if (s != 0.0f) {
+      for (int c = 0; c < kRowSteps; ++c)
+        if (c < nsteps) qrow[c] = convert_step(t, c);
+    } else {
+      for (int c = 0; c < nsteps; ++c) {
+        const u32x4 q = convert_step(t, c);
+        const int el = c * (kWave * 16) + lane * 16;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t lo = e4m3fn_sat_pair(f[4 * i] / s, f[4 * i + 1] / s);
-          const uint32_t hi = e4m3fn_sat_pair(f[4 * i + 2] / s, f[4 * i + 3] / s);
-          q[i] = lo | (hi << 16);
+        for (int j = 0; j < KMAX; ++j) {
+          if (d[j] < 0) continue;
+          if (el < H) nt_store(q, reinterpret_cast<u32x4*>(rbase + static_cast<int64_t>(d[j]) * a.stride + el));
         }
-      }
-      // this step's groups are c*8 .. c*8+7; group c*8+g goes to lane
-      // (c*8+g) % 64, which is lane (c%8)*8 + g, register slot c/8
-      const float sc = __shfl(s, (lane & 7) * 8, kWave);
-      const bool keep = (lane >> 3) == (c & 7);
-#pragma unroll
-      for (int r = 0; r < kMaxScaleSlots; ++r)
-        if (keep && r == (c >> 3)) my_sc[r] = sc;
-#pragma unroll
-      for (int j = 0; j < KMAX; ++j) {
-        if (d[j] < 0) continue;
-        if (act) nt_store(q, reinterpret_cast<u32x4*>(rbase + static_cast<int64_t>(d[j]) * a.stride + el));
       }
     }
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
       if (d[j] < 0) continue;
-      char* tail = rbase + static_cast<int64_t>(d[j]) * a.stride + H;
+      char* row = rbase + static_cast<int64_t>(d[j]) * a.stride;
+      if constexpr (ROWBUF) {
+#pragma unroll
+        for (int c = 0; c < kRowSteps; ++c) {
+          const int el = c * (kWave * 16) + lane * 16;
+          if (c < nsteps && el < H) nt_store(qrow[c], reinterpret_cast<u32x4*>(row + el));
+        }
+      }
+      char* tail = row + H;
 #pragma unroll
       for (int r = 0; r < kMaxScaleSlots; ++r) {
         const int g = r * kWave + lane;
@@ -215,10 +254,21 @@ hipError_t scatter_bf16_k(const ScatterArgs& a, int vb, hipStream_t s) {
   }
 }
 
+// The row burst pays where rows share 128-byte lines with their neighbours
+// (a pitch that is not a multiple of 128: each row starts and ends inside a
+// line, and writing a whole row at once lets those partial lines combine);
+// at a line-aligned pitch the step-by-step stores keep more waves resident
+// and measured faster (hidden 7168: 126 vs 146 us at the packed 7392-byte
+// pitch, 118 vs 112 us at 7424).
 template <int KMAX>
 hipError_t scatter_fp8_k(const ScatterArgs& a, int64_t row_bytes, hipStream_t s) {
-  constexpr auto kern = k_scatter_fp8<KMAX>;
-  kern<<<persistent_blocks<kern>(a.T), kBlock, 0, s>>>(a, row_bytes);
+  if (a.H <= 8 * kWave * 16 && a.stride % 128 != 0) {
+    constexpr auto kern = k_scatter_fp8<KMAX, true>;
+    kern<<<persistent_blocks<kern>(a.T), kBlock, 0, s>>>(a, row_bytes);
+  } else {
+    constexpr auto kern = k_scatter_fp8<KMAX, false>;
+    kern<<<persistent_blocks<kern>(a.T), kBlock, 0, s>>>(a, row_bytes);
+  }
   return hipGetLastError();
 }
 

@@ -238,8 +238,16 @@ def _special_fp8_rows(H=1024):
     return flat.reshape(-1, H)
 
 
-def test_dispatch_fp8_special_values():
-    xs = _special_fp8_rows()
+@pytest.mark.parametrize("H", [8320, 16384])
+def test_dispatch_fp8_wide_hidden(H):
+    """Rows wider than 8192 elements take the kernel's step-by-step store
+    path (8320: nine steps, the last one partly active)."""
+    _dispatch_case(W.Workload("fp8w", T=150, H=H, K=4, E=16, mask_p=0.1, seed=H), fp8=True)
+
+
+@pytest.mark.parametrize("H", [1024, 9216])
+def test_dispatch_fp8_special_values(H):
+    xs = _special_fp8_rows(H)
     T, H = xs.shape
     w = W.Workload("fp8s", T=T, H=H, K=2, E=4)
     x = torch.from_numpy(xs.view(np.int16)).view(torch.bfloat16)

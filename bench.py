@@ -256,6 +256,11 @@ def main(argv=None):
         help="comma-separated names of the extra timings to run (default: all)",
     )
     ap.add_argument(
+        "--no-graph",
+        action="store_true",
+        help="skip timing the step as a captured HIP graph",
+    )
+    ap.add_argument(
         "--no-cold",
         action="store_true",
         help="skip the cold-cache pass (a 1 GiB buffer is read before each step, so the "
@@ -348,6 +353,40 @@ def main(argv=None):
     wall = time.perf_counter() - t0
     gpu_state["after"] = smi_snapshot()
 
+    # the same step (layout, fp8 dispatch, combine) captured once in a HIP
+    # graph and replayed: every launch is recorded, only the host's per-launch
+    # work goes away
+    t_graph = []
+    if not args.no_graph:
+        def core_step():
+            ep.ep_layout(d_idx, E, out=L)
+            ep.ep_dispatch(x, L, fp8=True, out=recv8)
+            ep.ep_combine(y, L, d_wt, out=out)
+
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            core_step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            core_step()
+        torch.cuda.synchronize()
+        for _ in range(3):
+            graph.replay()
+        marks = []
+        for _ in range(args.steps):
+            g0 = torch.cuda.Event(enable_timing=True)
+            g1 = torch.cuda.Event(enable_timing=True)
+            g0.record(stream)
+            graph.replay()
+            g1.record(stream)
+            marks.append((g0, g1))
+        torch.cuda.synchronize()
+        t_graph = [a.elapsed_time(b) for a, b in marks]
+        del graph
+
     ev_cold = {k: [] for k in ev}
     if not args.no_cold:
         # cold caches: read 1 GiB before every step (outside the timed
@@ -392,6 +431,8 @@ def main(argv=None):
     }
     if t_bf16:
         ops["dispatch_bf16"] = stats(t_bf16, nb["dispatch_bf16"])
+    if t_graph:
+        ops["step_graph"] = stats(t_graph, nb["layout"] + nb["dispatch_fp8"] + nb["combine"])
     ops_cold = None
     if ev_cold["start"]:
         c_layout = ms("start", "layout", ev_cold)

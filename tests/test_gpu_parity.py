@@ -448,3 +448,32 @@ def test_grouped_workload_sampled():
     want = O.combine_grouped(ysub, idx.numpy()[toks], slot_r, wt.numpy()[toks], w.E, w.G)
     got = u16(out.index_select(0, torch.from_numpy(toks).to(DEV)))
     assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("mask_p", [0.0, 0.5])
+def test_round_trip_dispatch_then_unit_weight_combine(mask_p):
+    """Dispatch bf16 rows, then combine those very rows with unit weights:
+    each token comes back as the fp32 sum of K_eff copies of itself, which is
+    exactly K_eff * x when K_eff is 1, 2, 4 or 8 (+0 when it is 0), and equal
+    to the oracle's dispatch followed by its combine (top-8, then again with
+    half the selections masked)."""
+    say("round trip", mask_p)
+    w = W.Workload("rt", T=600, H=384, K=8, E=32, mask_p=mask_p, seed=41 + int(mask_p * 10))
+    idx, _ = W.make_routing(w)
+    x = W.make_x(w)
+    L = ep().ep_layout(idx.to(DEV), w.E)
+    recv = ep().ep_dispatch(x.to(DEV), L)
+    ones = torch.ones(w.T, w.K, dtype=torch.float32, device=DEV)
+    out = ep().ep_combine(recv, L, ones)
+    got = u16(out)
+    R = O.layout(idx.numpy(), w.E)
+    xs = u16(x)
+    rows = O.dispatch_bf16(xs, R["slot"], R["n_sel"])
+    want = O.combine(rows, R["slot"], np.ones((w.T, w.K), np.float32))
+    assert np.array_equal(got, want)
+    k_eff = (idx.numpy() >= 0).sum(axis=1)
+    assert (got[k_eff == 0] == 0).all()  # nothing selected: +0, not 0 * x
+    exact = np.isin(k_eff, [1, 2, 4, 8])
+    assert exact.any()
+    scaled = O.bf16_rne((O.bf16_to_f32(xs[exact]) * k_eff[exact, None]).astype(np.float32))
+    assert np.array_equal(got[exact], scaled)

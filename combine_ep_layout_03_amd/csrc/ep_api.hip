@@ -218,6 +218,8 @@ int ep_expert_gemm(const ep_problem_t* p, const ep_layout_t* L, const void* x,
   const int64_t pad = static_cast<int64_t>(p->num_experts) *
                       (p->expert_alignment > 1 ? p->expert_alignment - 1 : 0);
   const int64_t max_rows = p->num_tokens * p->topk + pad;
+  // the kernel numbers its tiles in int32
+  if (ep::expert_gemm_max_tiles(max_rows, p->num_experts, n_out) > INT32_MAX) return EP_ENOTSUP;
   return ep::launch_expert_gemm(a, max_rows, stream) == hipSuccess ? EP_OK : EP_EHIP;
 }
 

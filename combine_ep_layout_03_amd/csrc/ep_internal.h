@@ -101,6 +101,8 @@ struct GemmArgs {
 };
 // H % 64 == 0, N % 128 == 0, E <= 1024, 16-byte aligned x / w / y and strides
 // (ldx % 8 == 0, ldy % 4 == 0); max_rows bounds the expert-major rows.
+// upper bound on the grouped GEMM's tiles for max_rows receive rows
+int64_t expert_gemm_max_tiles(int64_t max_rows, int E, int N);
 hipError_t launch_expert_gemm(const GemmArgs& a, int64_t max_rows, hipStream_t s);
 
 }  // namespace ep

@@ -236,9 +236,10 @@ int ep_combine(const ep_problem_t* p, const ep_layout_t* L, const int64_t* topk_
  *   w  bf16 [E, n_out, H]: expert e's n_out output rows, each H long;
  *   y  bf16 output rows, row r at element r * y_row_stride (0 = n_out).
  * Rows outside every expert's selections (alignment padding, rows past the
- * layout) are not written.  Requires H % 64 == 0 and n_out % 128 == 0
- * (EP_ENOTSUP otherwise), 16-byte aligned x, w and y, x_row_stride a
- * multiple of 8 and y_row_stride a multiple of 4. */
+ * layout) are not written.  Requires H % 64 == 0 and n_out % 128 == 0, and
+ * at most 2^31 - 1 output tiles of 320 x 256 (EP_ENOTSUP otherwise), 16-byte
+ * aligned x, w and y, x_row_stride a multiple of 8 and y_row_stride a
+ * multiple of 4. */
 int ep_expert_gemm(const ep_problem_t* p, const ep_layout_t* L, const void* x,
                    int64_t x_row_stride, const void* w, int32_t n_out, void* y,
                    int64_t y_row_stride, hipStream_t stream);

@@ -91,6 +91,31 @@ def test_invalid_arguments_return_codes_before_any_launch():
     assert L.ep_combine(ctypes.byref(p0), ctypes.byref(lay), None, None, None, 0, None, None, None, 0, None) == _lib.EP_OK
 
 
+def test_expert_gemm_host_checks():
+    """The grouped GEMM's shape limits are checked on the host, before any
+    pointer is used or any kernel launched (the pointers below are aligned
+    placeholders that are never dereferenced)."""
+    from combine_ep_layout_03_amd import _lib
+
+    L = _lib.lib()
+    lay = _lib.LayoutStruct()
+    lay.counts = 256
+    lay.offsets = 256
+    fake = ctypes.c_void_p(1 << 20)
+    p = _lib.Problem(1 << 20, 7168, 8, 1024, 0, 0, 0)
+    # hidden % 64 and n_out % 128
+    bad_h = _lib.Problem(16, 7168 + 32, 8, 256, 0, 0, 0)
+    assert L.ep_expert_gemm(ctypes.byref(bad_h), ctypes.byref(lay), fake, 0, fake, 2048, fake, 0, None) == _lib.EP_ENOTSUP
+    assert L.ep_expert_gemm(ctypes.byref(p), ctypes.byref(lay), fake, 0, fake, 2048 + 64, fake, 0, None) == _lib.EP_ENOTSUP
+    # more output tiles than the kernel can number
+    assert L.ep_expert_gemm(ctypes.byref(p), ctypes.byref(lay), fake, 0, fake, 1 << 30, fake, 0, None) == _lib.EP_ENOTSUP
+    # a row stride below the row size, or misaligned
+    assert L.ep_expert_gemm(ctypes.byref(p), ctypes.byref(lay), fake, 7000, fake, 2048, fake, 0, None) == _lib.EP_EINVAL
+    assert L.ep_expert_gemm(ctypes.byref(p), ctypes.byref(lay), fake, 7172, fake, 2048, fake, 0, None) == _lib.EP_EINVAL
+    # misaligned base
+    assert L.ep_expert_gemm(ctypes.byref(p), ctypes.byref(lay), ctypes.c_void_p((1 << 20) + 8), 0, fake, 2048, fake, 0, None) == _lib.EP_EINVAL
+
+
 def test_binding_rejects_host_tensors():
     import torch
 

@@ -128,6 +128,8 @@ def time_extras(ep, W, w, d_idx, d_wt, x, y, L, n_sel, rb, pitch, reps, only=Non
     # grouped GEMM consumer: receive rows @ per-expert weights, H -> 2048
     N = 2048
     if only is not None and "expert_gemm_bf16_n2048" not in only:
+        if "grouped_t65536_g8" in only:
+            res["grouped_t65536_g8"] = time_grouped_receive_share(ep, W, dev, stream, max(3, reps // 5))
         ep.ep_layout(d_idx, E, out=L)
         return res
     xr = W.make_rows(w, L.max_expert_rows(), device=dev)
@@ -157,11 +159,65 @@ def time_extras(ep, W, w, d_idx, d_wt, x, y, L, n_sel, rb, pitch, reps, only=Non
         "traffic": counted_traffic("expert_gemm_n2048", w.name),
     }
     del xr, wts, yg
+    if only is None or "grouped_t65536_g8" in only:
+        res["grouped_t65536_g8"] = time_grouped_receive_share(ep, W, dev, stream, max(3, reps // 5))
     res["_note"] = (
         f"grouped rows R={R} ({R / T:.3f} per token); aligned expert rows {n_al} "
         f"(of which {n_al - n_sel} padding, counted as written bytes)"
     )
     ep.ep_layout(d_idx, E, out=L)  # restore the headline layout
+    return res
+
+
+def time_grouped_receive_share(ep, W, dev, stream, reps):
+    """One GPU's receive share with grouped dedup at its real size: 65536
+    source tokens x 7168, top-8 of 256 experts in 8 groups of 32.  Times the
+    grouped layout, the bf16 dispatch of one row per (token, group hit) and
+    the grouped-order combine over one expert-output row per selection."""
+    import torch
+
+    w = W.by_name("grouped")
+    T, H, K, E, G = w.T, w.H, w.K, w.E, w.G
+    gi, gw = W.make_routing(w, device=dev)
+    gx = W.make_x(w, device=dev)
+    gy = W.make_y(w, device=dev)
+    LG = ep.ep_layout(gi, E, G, gw)
+    R = LG.num_rows(ep.EP_ROWS_GROUP)
+    n_sel = LG.num_rows()
+    recv = torch.empty(R, H, dtype=torch.bfloat16, device=dev)
+    out = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    cases = {
+        # ids and weights read; slot and group row written per selection;
+        # source token and K-wide id / weight lists written per row
+        "layout": (lambda: ep.ep_layout(gi, E, G, gw, out=LG), T * K * (8 + 4 + 4 + 4) + R * (4 + K * 8)),
+        "dispatch_bf16_group_rows": (
+            lambda: ep.ep_dispatch(gx, LG, rows=ep.EP_ROWS_GROUP, out=recv, capacity=R),
+            T * H * 2 + T * K * 4 + R * H * 2,
+        ),
+        "combine_grouped": (
+            lambda: ep.ep_combine(gy, LG, gw, gi, order=ep.EP_COMBINE_GROUPED, out=out),
+            n_sel * H * 2 + T * K * (4 + 4 + 8) + T * H * 2,
+        ),
+    }
+    res = {"rows_R": int(R), "selections": int(n_sel)}
+    for name, (fn, nbytes) in cases.items():
+        fn()
+        a0 = torch.cuda.Event(enable_timing=True)
+        a1 = torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        for _ in range(reps):
+            fn()
+        a1.record(stream)
+        torch.cuda.synchronize()
+        us = a0.elapsed_time(a1) * 1e3 / reps
+        res[name] = {
+            "us": round(us, 1),
+            "bytes": int(nbytes),
+            "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "pct_of_peak": round(100.0 * nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
+        }
+    del gx, gy, recv, out, LG
+    torch.cuda.empty_cache()
     return res
 
 

@@ -334,7 +334,7 @@ def main(argv=None):
     if args.gpus != 1:
         print(
             f"bench.py measures one GPU's share of dispatch/combine; --gpus {args.gpus} is not "
-            "supported (no collectives in this build)",
+            "supported (the library has no collectives)",
             file=sys.stderr,
         )
         return 2

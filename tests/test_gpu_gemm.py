@@ -53,6 +53,7 @@ def _check(got_u16, x_u16, counts, offsets, w_u16, rows=None):
         (700, 3, 12, 192, 384, 64),
         (90, 2, 4, 64, 128, 0),  # two reduction steps: fewer than the ring's depth
         (1500, 2, 4, 320, 256, 0),  # ~750 rows per expert: three row tiles each
+        (600, 2, 1024, 64, 128, 0),  # the largest expert count, most experts empty
     ],
 )
 def test_expert_gemm_small(T, K, E, H, N, A):

@@ -90,6 +90,8 @@ def test_layout_workloads(name):
         (20000, 8, 256, 8, 0.05),  # several rounds per block
         (3000, 32, 512, 16, 0.0),  # K at the limit
         (2000, 4, 1000, 0, 0.0),  # E near the key limit
+        (2000, 4, 1024, 0, 0.0),  # E + G at the key limit
+        (2000, 4, 992, 32, 0.1),  # E + G at the key limit, grouped
     ],
 )
 def test_layout_edge_shapes(T, K, E, G, mask):
@@ -238,11 +240,13 @@ def _special_fp8_rows(H=1024):
     return flat.reshape(-1, H)
 
 
-@pytest.mark.parametrize("H", [8320, 16384])
+@pytest.mark.parametrize("H", [8320, 16384, 32768])
 def test_dispatch_fp8_wide_hidden(H):
     """Rows wider than 8192 elements take the kernel's step-by-step store
-    path (8320: nine steps, the last one partly active)."""
-    _dispatch_case(W.Workload("fp8w", T=150, H=H, K=4, E=16, mask_p=0.1, seed=H), fp8=True)
+    path (8320: nine steps, the last one partly active; 32768: the largest
+    supported row, 256 scale groups)."""
+    T = 150 if H < 32768 else 60
+    _dispatch_case(W.Workload("fp8w", T=T, H=H, K=4, E=16, mask_p=0.1, seed=H), fp8=True)
 
 
 @pytest.mark.parametrize("H", [1024, 9216])

@@ -23,6 +23,13 @@ SOURCES = ["ep_api.hip", "ep_layout.hip", "ep_dispatch.hip", "ep_combine.hip", "
 TEST_SOURCE = os.path.join(ROOT, "tests", "hip", "e4m3_check.hip")
 TEST_LIB_PATH = os.path.join(ROOT, "tests", "hip", "libep_e4m3_check.so")
 
+# plain-C consumer of the C ABI (tests/c), built with the host C compiler
+C_EXAMPLE_SOURCE = os.path.join(ROOT, "tests", "c", "ep_c_roundtrip.c")
+C_EXAMPLE_PATH = os.path.join(ROOT, "tests", "c", "ep_c_roundtrip")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+# what a C (not HIP) translation unit needs to include the HIP runtime API
+C_HIP_FLAGS = ["-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROCM, "include")]
+
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
@@ -75,6 +82,26 @@ def build_test_lib(verbose: bool = False) -> str:
     return TEST_LIB_PATH
 
 
+def build_c_example(verbose: bool = False) -> str:
+    """Compile the C99 program that drives the library through the header
+    alone (layout, dispatch, combine); links the in-tree library by rpath."""
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        raise RuntimeError("no C compiler found for the C-ABI example")
+    tmp = C_EXAMPLE_PATH + ".tmp"
+    cmd = [cc, "-std=c99", "-O2", "-Wall", "-Wextra", *C_HIP_FLAGS, "-I", INCLUDE, C_EXAMPLE_SOURCE,
+           "-o", tmp, "-L", HERE, "-lep_mi355x", "-L", os.path.join(ROCM, "lib"), "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/../../combine_ep_layout_03_amd", "-Wl,-rpath," + os.path.join(ROCM, "lib")]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"C build failed ({res.returncode}):\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, C_EXAMPLE_PATH)
+    return C_EXAMPLE_PATH
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
     print(build_test_lib(verbose=True))
+    print(build_c_example(verbose=True))

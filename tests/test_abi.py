@@ -22,6 +22,40 @@ def test_header_declares_the_boundary():
     )
 
 
+def test_header_compiles_as_c99():
+    """The header is plain C: a C99 translation unit that includes it and
+    calls every entry point compiles with gcc (no C++ in the boundary)."""
+    import shutil
+    import subprocess
+    import tempfile
+
+    from combine_ep_layout_03_amd import build as b
+
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = """#include "ep_mi355x.h"
+int use(void) {
+  ep_problem_t p = {0};
+  ep_layout_t l = {0};
+  (void)ep_fp8_row_bytes(128); (void)ep_layout_workspace_bytes(&p);
+  (void)ep_layout(&p, 0, 0, &l, 0, 0, 0); (void)ep_dispatch(&p, &l, 0, 0, 0, 0, 0, 0, 0);
+  (void)ep_combine(&p, &l, 0, 0, 0, 0, 0, 0, 0, 0, 0);
+  (void)ep_expert_gemm(&p, &l, 0, 0, 0, 0, 0, 0, 0); (void)ep_strerror(0);
+  return 0;
+}
+"""
+    with tempfile.TemporaryDirectory() as d:
+        path = os.path.join(d, "use.c")
+        open(path, "w").write(src)
+        res = subprocess.run(
+            [cc, "-std=c99", "-Wall", "-Werror=implicit-function-declaration", "-fsyntax-only",
+             *b.C_HIP_FLAGS, "-I", os.path.join(ROOT, "include"), path],
+            capture_output=True, text=True,
+        )
+    assert res.returncode == 0, res.stderr
+
+
 def test_library_exports_every_declared_symbol():
     from combine_ep_layout_03_amd import _lib
 

@@ -255,3 +255,28 @@ def test_group_order_is_ascending():
     w = np.ones((1, 3), np.float32)
     assert np.all(O.bf16_to_f32(O.combine_grouped(y, idx, L["slot"], w, 6, 3)) == 1.0)
     assert np.all(O.bf16_to_f32(O.combine(y, L["slot"], w)) == 0.0)
+
+
+def test_fp8_quotient_is_a_true_division():
+    """The fp8 quotient is the IEEE fp32 division x / s (reading of the
+    spec formula), not x * (1 / s): for this bf16 group the exact
+    quotient rounds to fp32 84.0, the midpoint between the E4M3 values 80
+    and 88, so ties-to-even gives 80 (code 0x6A).  The product with the
+    rounded reciprocal is 84.0000076, which would encode as 88 (0x6B)."""
+    from fractions import Fraction
+
+    a = O.bf16_to_f32(np.array([0x3D98], np.uint16))[0]  # the group's amax
+    xv = O.bf16_to_f32(np.array([0x3C64], np.uint16))[0]
+    s = np.float32(Fraction(float(a)) / 448)  # exact a/448 rounded once to fp32
+    # the exact quotient, rounded to the nearest fp32 by comparing neighbours
+    q = Fraction(float(xv)) / Fraction(float(s))
+    c = np.float32(float(q))
+    cands = [np.nextafter(c, np.float32(0)), c, np.nextafter(c, np.float32(np.inf))]
+    nearest = min(cands, key=lambda f: abs(Fraction(float(f)) - q))
+    assert nearest == np.float32(84.0)
+    g = np.zeros(128, np.uint16)
+    g[0], g[1] = 0x3D98, 0x3C64
+    row = O.quantize_row_fp8(g)
+    assert row[0] == 0x7E  # the amax element encodes to 448
+    assert row[1] == 0x6A  # 80: the tie at 84 goes to the even code
+    assert np.frombuffer(row[128:132].tobytes(), "<f4")[0] == s

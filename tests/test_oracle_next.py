@@ -142,3 +142,42 @@ def test_expert_gemm_bruteforce_and_segments():
             got[r] = O.bf16_to_f32(O.bf16_rne(np.array([acc], np.float32)))[0]
     ok = ~np.isnan(y[:, 0])
     assert np.all(np.abs(got[ok] - y[ok, 0]) <= b[ok, 0])
+
+
+def test_bias_seeds_the_accumulator_not_added_after():
+    """The bias starts the fp32 sum (the reading of "seeds the reduce
+    accumulator"): with bias -1 and terms 1 and 2^-30 the seeded flat sum is
+    (-1 + 1) + 2^-30 = 2^-30, while adding the bias after the terms would
+    give (1 + 2^-30) - 1 = 0 in fp32."""
+    one = O.bf16_rne(np.array([1.0], np.float32))[0]
+    tiny = O.bf16_rne(np.array([2.0**-30], np.float32))[0]
+    minus_one = O.bf16_rne(np.array([-1.0], np.float32))[0]
+    y = np.array([[one], [tiny]], np.uint16)
+    slot = np.array([[0, 1]])
+    w = np.ones((1, 2), np.float32)
+    out = O.combine(y, slot, w, bias0=np.array([[minus_one]], np.uint16))
+    assert out[0, 0] == tiny
+    # grouped order: the bias seeds the cross-group total, each group's
+    # partial starts from +0.  Two groups: (-1 + 1) + 2^-30 = 2^-30; one
+    # group: -1 + (1 + 2^-30 -> 1) = +0.
+    b = np.array([[minus_one]], np.uint16)
+    assert O.combine_grouped(y, np.array([[0, 1]]), slot, w, 2, 2, bias0=b)[0, 0] == tiny
+    assert O.combine_grouped(y, np.array([[0, 1]]), slot, w, 2, 1, bias0=b)[0, 0] == 0x0000
+
+
+def test_gemm_bound_covers_fp32_cancellation():
+    """The bound's accumulation term matters: the fp32 sum in k order of
+    2^20 + 2^-5 - 2^20 is 0 (2^-5 is lost against 2^20), the exact value
+    2^-5; the bf16 rounding term alone (2^-8 |y|) would not cover that."""
+    vals = [2.0**20, 2.0**-5, -(2.0**20)]
+    x = O.bf16_rne(np.ones((1, 3), np.float32))
+    w = O.bf16_rne(np.array([[vals]], np.float32))  # [E=1, N=1, H=3]
+    y64 = O.expert_gemm(x, np.array([1]), np.array([0, 1]), w)
+    assert y64[0, 0] == 2.0**-5
+    acc = np.float32(0.0)
+    for v in vals:
+        acc = np.float32(acc + np.float32(v))
+    assert acc == 0.0
+    b = O.expert_gemm_bound(x, np.array([1]), np.array([0, 1]), w, y64)
+    assert abs(float(acc) - y64[0, 0]) <= b[0, 0]
+    assert abs(float(acc) - y64[0, 0]) > abs(y64[0, 0]) * 2.0**-8

@@ -125,42 +125,69 @@ def time_extras(ep, W, w, d_idx, d_wt, x, y, L, n_sel, rb, pitch, reps, only=Non
             "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
             "pct_of_peak": round(100.0 * nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
         }
+    def want(name):
+        return only is None or name in only
+
     # grouped GEMM consumer: receive rows @ per-expert weights, H -> 2048
     N = 2048
-    if only is not None and "expert_gemm_bf16_n2048" not in only:
-        if "grouped_t65536_g8" in only:
-            res["grouped_t65536_g8"] = time_grouped_receive_share(ep, W, dev, stream, max(3, reps // 5))
-        ep.ep_layout(d_idx, E, out=L)
-        return res
-    xr = W.make_rows(w, L.max_expert_rows(), device=dev)
-    wts = W.make_expert_weights(w, N, device=dev)
-    yg = torch.empty(xr.shape[0], N, dtype=torch.bfloat16, device=dev)
-    fn = lambda: ep.ep_expert_gemm(xr, L, wts, out=yg)  # noqa: E731
-    fn()
-    a0 = torch.cuda.Event(enable_timing=True)
-    a1 = torch.cuda.Event(enable_timing=True)
     gemm_reps = max(3, reps // 5)
-    a0.record(stream)
-    for _ in range(gemm_reps):
-        fn()
-    a1.record(stream)
-    torch.cuda.synchronize()
-    us = a0.elapsed_time(a1) * 1e3 / gemm_reps
     flops = 2.0 * n_sel * H * N
-    nbytes = E * N * H * 2 + n_sel * H * 2 + n_sel * N * 2
-    res["expert_gemm_bf16_n2048"] = {
-        "us": round(us, 1),
-        "TFLOPs": round(flops / (us * 1e-6) / 1e12, 1),
-        "pct_of_mfma_peak": round(100.0 * flops / (us * 1e-6) / 2.5e15, 1),
-        "bytes": int(nbytes),
-        "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
-        "pct_of_hbm_peak": round(100.0 * nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
-        "bound_us": {"mfma": round(flops / 2.5e15 * 1e6, 1), "hbm": round(nbytes / 8e12 * 1e6, 1)},
-        "traffic": counted_traffic("expert_gemm_n2048", w.name),
-    }
-    del xr, wts, yg
-    if only is None or "grouped_t65536_g8" in only:
-        res["grouped_t65536_g8"] = time_grouped_receive_share(ep, W, dev, stream, max(3, reps // 5))
+
+    def timed(fn, n):
+        fn()
+        b0 = torch.cuda.Event(enable_timing=True)
+        b1 = torch.cuda.Event(enable_timing=True)
+        b0.record(stream)
+        for _ in range(n):
+            fn()
+        b1.record(stream)
+        torch.cuda.synchronize()
+        return b0.elapsed_time(b1) * 1e3 / n
+
+    if want("expert_gemm_bf16_n2048") or want("expert_gemm_fused_dispatch_n2048"):
+        wts = W.make_expert_weights(w, N, device=dev)
+        yg = torch.empty(L.max_expert_rows(), N, dtype=torch.bfloat16, device=dev)
+        if want("expert_gemm_bf16_n2048"):
+            xr = W.make_rows(w, L.max_expert_rows(), device=dev)
+            us = timed(lambda: ep.ep_expert_gemm(xr, L, wts, out=yg), gemm_reps)
+            nbytes = E * N * H * 2 + n_sel * H * 2 + n_sel * N * 2
+            res["expert_gemm_bf16_n2048"] = {
+                "us": round(us, 1),
+                "TFLOPs": round(flops / (us * 1e-6) / 1e12, 1),
+                "pct_of_mfma_peak": round(100.0 * flops / (us * 1e-6) / 2.5e15, 1),
+                "bytes": int(nbytes),
+                "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                "pct_of_hbm_peak": round(100.0 * nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
+                "bound_us": {"mfma": round(flops / 2.5e15 * 1e6, 1), "hbm": round(nbytes / 8e12 * 1e6, 1)},
+                "traffic": counted_traffic("expert_gemm_n2048", w.name),
+            }
+            del xr
+        if want("expert_gemm_fused_dispatch_n2048"):
+            # the same GEMM with the dispatch folded into its loads (rows
+            # gathered from the token matrix through expert_row_src), against
+            # bf16 dispatch followed by the GEMM on the receive rows
+            Lf = ep.ep_layout(d_idx, E, expert_row_src=True)
+            recv16 = torch.empty(Lf.max_expert_rows(), H, dtype=torch.bfloat16, device=dev)
+
+            def unfused():
+                ep.ep_dispatch(x, Lf, out=recv16)
+                ep.ep_expert_gemm(recv16, Lf, wts, out=yg)
+
+            us_f = timed(lambda: ep.ep_expert_gemm(x, Lf, wts, out=yg, gather=True), gemm_reps)
+            us_u = timed(unfused, gemm_reps)
+            fbytes = E * N * H * 2 + T * H * 2 + n_sel * N * 2
+            res["expert_gemm_fused_dispatch_n2048"] = {
+                "us": round(us_f, 1),
+                "us_dispatch_then_gemm": round(us_u, 1),
+                "TFLOPs": round(flops / (us_f * 1e-6) / 1e12, 1),
+                "bytes": int(fbytes),
+                "GBps": round(fbytes / (us_f * 1e-6) / 1e9, 1),
+                "pct_of_hbm_peak": round(100.0 * fbytes / (us_f * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
+            }
+            del recv16, Lf
+        del wts, yg
+    if want("grouped_t65536_g8"):
+        res["grouped_t65536_g8"] = time_grouped_receive_share(ep, W, dev, stream, gemm_reps)
     res["_note"] = (
         f"grouped rows R={R} ({R / T:.3f} per token); aligned expert rows {n_al} "
         f"(of which {n_al - n_sel} padding, counted as written bytes)"

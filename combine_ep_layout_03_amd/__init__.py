@@ -405,11 +405,16 @@ def ep_expert_gemm(
     layout: Layout,
     w: torch.Tensor,
     out: torch.Tensor | None = None,
+    gather: bool = False,
 ) -> torch.Tensor:
-    """Grouped GEMM over the expert-major segments: y[r] = x[r] @ w[e]^T for
-    each receive row r of expert e.  x: bf16 [rows, >= H] (row pitch = its
-    row size); w: bf16 [E, N, H]; returns y bf16 [rows, N] (rows outside the
-    experts' selections are left as they were)."""
+    """Grouped GEMM over the expert-major segments: y[r] = x_r @ w[e]^T for
+    each receive row r of expert e; w: bf16 [E, N, H]; returns y bf16
+    [rows, N] (rows outside the experts' selections are left as they were).
+
+    x_r is row r of x (bf16 [rows, >= H], the dispatched receive rows), or,
+    with ``gather``, row expert_row_src[r] of the token matrix x (bf16
+    [T, >= H]): the dispatch folded into the GEMM's loads, which needs a
+    layout computed with ``expert_row_src=True``."""
     layout = _resolve(layout)
     if x.dim() != 2 or w.dim() != 3:
         raise ValueError("x must be [rows, H] and w [E, N, H]")
@@ -420,15 +425,23 @@ def ep_expert_gemm(
     _dev(w, "w", torch.bfloat16)
     if x.shape[1] < H:
         raise ValueError("x rows are shorter than H")
+    rows = layout.max_expert_rows()
+    if gather:
+        if x.shape[0] != layout.num_tokens:
+            raise ValueError("with gather, x must be the [T, H] token matrix")
+        if layout.expert_row_src is None or layout.expert_row_capacity < rows:
+            raise ValueError("gather needs a layout computed with expert_row_src=True")
+    elif x.shape[0] < rows:
+        raise ValueError("x must hold the layout's worst-case expert rows")
     if out is None:
-        out = torch.empty(x.shape[0], N, dtype=torch.bfloat16, device=x.device)
+        out = torch.empty(rows if gather else x.shape[0], N, dtype=torch.bfloat16, device=x.device)
     else:
         _dev(out, "out", torch.bfloat16)
-        if out.dim() != 2 or out.shape[1] < N or out.shape[0] < x.shape[0]:
-            raise ValueError("out must be bf16 [>= rows, >= N]")
-    if x.shape[0] < layout.max_expert_rows():
-        raise ValueError("x must hold the layout's worst-case expert rows")
-    p = _problem(layout.num_tokens, H, layout.topk, layout.num_experts, layout.num_groups, layout.expert_alignment)
+        if out.dim() != 2 or out.shape[1] < N or out.shape[0] < rows:
+            raise ValueError("out must be bf16 [>= expert rows, >= N]")
+    flags = _lib.EP_FLAG_GATHER_ROWS if gather else 0
+    p = _problem(layout.num_tokens, H, layout.topk, layout.num_experts, layout.num_groups,
+                 layout.expert_alignment, flags)
     s = layout.struct()
     rc = _lib.lib().ep_expert_gemm(
         ctypes.byref(p), ctypes.byref(s), _ptr(x), int(x.shape[1]), _ptr(w), int(N), _ptr(out), int(out.shape[1]),

@@ -31,6 +31,7 @@ EP_STATUS_SELECTIONS = 6
 EP_STATUS_WORDS = 8
 
 EP_FLAG_ZERO_PADDING = 1
+EP_FLAG_GATHER_ROWS = 2
 
 EP_FORMAT_BF16 = 0
 EP_FORMAT_FP8_PACKED = 1

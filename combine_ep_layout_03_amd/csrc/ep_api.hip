@@ -18,7 +18,7 @@ int check_problem(const ep_problem_t* p) {
     return EP_EINVAL;
   if (p->num_groups > 0 && p->num_experts % p->num_groups != 0) return EP_EINVAL;
   if (p->expert_alignment < 0 || p->expert_alignment > (1 << 20)) return EP_EINVAL;
-  if (p->flags & ~EP_FLAG_ZERO_PADDING) return EP_EINVAL;
+  if (p->flags & ~(EP_FLAG_ZERO_PADDING | EP_FLAG_GATHER_ROWS)) return EP_EINVAL;
   if (p->topk > EP_MAX_TOPK) return EP_ENOTSUP;
   if (static_cast<int64_t>(p->num_experts) + p->num_groups > EP_MAX_KEYS) return EP_ENOTSUP;
   // slots and rows are int32: every (t,k) row, padding included, must index below 2^31
@@ -218,6 +218,13 @@ int ep_expert_gemm(const ep_problem_t* p, const ep_layout_t* L, const void* x,
   const int64_t pad = static_cast<int64_t>(p->num_experts) *
                       (p->expert_alignment > 1 ? p->expert_alignment - 1 : 0);
   const int64_t max_rows = p->num_tokens * p->topk + pad;
+  a.row_src = nullptr;
+  if (p->flags & EP_FLAG_GATHER_ROWS) {
+    // token rows gathered through the layout's expert-row map, which must
+    // cover every expert row the layout can produce
+    if (!L->expert_row_src || L->expert_row_capacity < max_rows) return EP_EINVAL;
+    a.row_src = L->expert_row_src;
+  }
   // the kernel numbers its tiles in int32
   if (ep::expert_gemm_max_tiles(max_rows, p->num_experts, n_out) > INT32_MAX) return EP_ENOTSUP;
   return ep::launch_expert_gemm(a, max_rows, stream) == hipSuccess ? EP_OK : EP_EHIP;

@@ -40,6 +40,11 @@
 // expert, column-tile major, row-tile minor).  Blocks are dealt to the 8
 // XCDs round-robin by block index, so each XCD takes a contiguous run of
 // tiles: the column tiles sharing an expert's rows then meet in one L2.
+//
+// With rows gathered, x is the token matrix and each expert row's operand is
+// loaded from the token the layout recorded for it, so the dispatch's scatter
+// happens inside the GEMM's loads (the mKernel article's fused MoE dispatch
+// and grouped GEMM): no receive buffer is written or read.
 #include "ep_device.h"
 #include "ep_internal.h"
 
@@ -157,7 +162,10 @@ __global__ __launch_bounds__(kThreads) void k_expert_gemm(GemmArgs a) {
     const int kv = (s & 3) ^ ((r >> 2) & 3);
     if (xwave) {
       const int xr = r < nrows ? r : 0;
-      src[q] = a.x + static_cast<int64_t>(row0 + xr) * a.ldx + kv * 8;
+      // expert row -> the x row holding its operand: itself, or (rows
+      // gathered) the token it came from
+      const int64_t xrow = a.row_src ? a.row_src[row0 + xr] : row0 + xr;
+      src[q] = a.x + xrow * a.ldx + kv * 8;
     } else {
       const int wr = n0 + r < a.N ? r : 0;  // the last column tile may be half valid
       src[q] = a.w + (static_cast<int64_t>(e) * a.N + n0 + wr) * a.H + kv * 8;

@@ -98,6 +98,9 @@ struct GemmArgs {
   const int32_t* offsets;
   int E, H, N;
   int ntn;  // column tiles, ceil(N / 256)
+  // null: x holds the expert rows; else x holds token rows and expert row r
+  // reads x row row_src[r]
+  const int32_t* row_src;
 };
 // H % 64 == 0, N % 128 == 0, E <= 1024, 16-byte aligned x / w / y and strides
 // (ldx % 8 == 0, ldy % 4 == 0); max_rows bounds the expert-major rows.

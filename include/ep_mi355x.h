@@ -67,6 +67,7 @@ extern "C" {
 
 /* ---- problem flags ---------------------------------------------------- */
 #define EP_FLAG_ZERO_PADDING 1 /* dispatch zeroes the alignment padding rows */
+#define EP_FLAG_GATHER_ROWS 2  /* ep_expert_gemm reads token rows through expert_row_src */
 
 /* ---- formats, row kinds, combine orders ------------------------------ */
 #define EP_FORMAT_BF16 0       /* receive row = the token's H bf16 values */
@@ -94,7 +95,11 @@ extern "C" {
  *               consume (PR commit adding do_expand: expert_alignment).  The
  *               rows past an expert's selections are padding.
  *   flags       EP_FLAG_ZERO_PADDING: ep_dispatch also zeroes every byte of
- *               the padding rows' row size (the PR's zero_padding). */
+ *               the padding rows' row size (the PR's zero_padding).
+ *               EP_FLAG_GATHER_ROWS: ep_expert_gemm takes the token rows
+ *               themselves and gathers each expert row's operand through
+ *               the layout's expert_row_src (dispatch fused into the GEMM).
+ *               Other entry points ignore it. */
 typedef struct ep_problem {
   int64_t num_tokens;
   int32_t hidden;
@@ -236,7 +241,15 @@ int ep_combine(const ep_problem_t* p, const ep_layout_t* L, const int64_t* topk_
  *   w  bf16 [E, n_out, H]: expert e's n_out output rows, each H long;
  *   y  bf16 output rows, row r at element r * y_row_stride (0 = n_out).
  * Rows outside every expert's selections (alignment padding, rows past the
- * layout) are not written.  Requires H % 64 == 0 and n_out % 128 == 0, and
+ * layout) are not written.
+ * With EP_FLAG_GATHER_ROWS in p->flags, x is instead the token matrix
+ * (bf16 [T, H], row t at element t * x_row_stride) and expert row r reads
+ * x row expert_row_src[r]: the dispatch's scatter folded into the GEMM's
+ * operand loads, as the mKernel article's fused MoE dispatch + grouped GEMM
+ * runs the GEMM on rows as they arrive, with no staging copy.  L must then
+ * carry expert_row_src (from ep_layout) with expert_row_capacity covering
+ * every expert row; the result equals the unfused dispatch + GEMM bit for
+ * bit.  Requires H % 64 == 0 and n_out % 128 == 0, and
  * at most 2^31 - 1 output tiles of 320 x 256 (EP_ENOTSUP otherwise), 16-byte
  * aligned x, w and y, x_row_stride a multiple of 8 and y_row_stride a
  * multiple of 4. */

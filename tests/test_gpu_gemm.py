@@ -143,3 +143,50 @@ def test_expert_gemm_pages_shape_sampled():
     ys = u16(y.index_select(0, sel))
     rel = _check(ys, xs, sub_counts, sub_offsets, ws)
     print("rel_l2", rel, flush=True)
+
+
+@pytest.mark.parametrize(
+    "name,T,K,E,H,N,A",
+    [
+        ("gf1", 300, 2, 8, 256, 256, 0),
+        ("gf2", 700, 3, 12, 192, 384, 64),  # aligned segments with padding rows
+        ("gf3", 1500, 2, 4, 320, 256, 0),   # several row tiles per expert
+    ],
+)
+def test_gathered_gemm_equals_dispatch_then_gemm(name, T, K, E, H, N, A):
+    """Rows gathered through expert_row_src inside the GEMM (dispatch fused
+    into the GEMM's loads) give exactly the dispatch-then-GEMM result: same
+    operands, same accumulation order.  The first case is also checked
+    against the oracle's bound."""
+    w = W.Workload(name, T=T, H=H, K=K, E=E, mask_p=0.1, seed=T + H)
+    idx, _ = W.make_routing(w)
+    L = ep().ep_layout(idx.to(DEV), E, expert_alignment=A, expert_row_src=True)
+    x = W.make_x(w).to(DEV)
+    wts = W.make_expert_weights(w, N).to(DEV)
+    recv = ep().ep_dispatch(x, L)
+    y_unfused = ep().ep_expert_gemm(recv, L, wts)
+    y_fused = ep().ep_expert_gemm(x, L, wts, gather=True)
+    torch.cuda.synchronize()
+    R = O.layout(idx.numpy(), E, expert_alignment=A)
+    n = len(R["expert_row_src"])
+    valid = R["expert_row_src"] >= 0
+    assert np.array_equal(u16(y_fused)[:n][valid], u16(y_unfused)[:n][valid])
+    if name == "gf1":
+        rows = O.dispatch_bf16(u16(x), R["slot"], R["n_rows_expert"])
+        _check(u16(y_fused)[:n], rows, R["counts"], R["offsets"], u16(wts))
+
+
+def test_gathered_gemm_pages_shape_equals_unfused():
+    """8192 tokens x top-8 of 256, H = 7168 -> N = 2048: the fused gather
+    equals dispatch then GEMM on every one of the 65536 expert rows."""
+    w = W.by_name("pages")
+    idx, _ = W.make_routing(w)
+    L = ep().ep_layout(idx.to(DEV), w.E, expert_row_src=True)
+    x = W.make_x(w, device=DEV)
+    wts = W.make_expert_weights(w, 2048, device=DEV)
+    print("gathered gemm pages shape: run", flush=True)
+    y_unfused = ep().ep_expert_gemm(ep().ep_dispatch(x, L), L, wts)
+    y_fused = ep().ep_expert_gemm(x, L, wts, gather=True)
+    torch.cuda.synchronize()
+    n = L.num_rows()
+    assert torch.equal(y_fused[:n].view(torch.int16), y_unfused[:n].view(torch.int16))

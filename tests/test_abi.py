@@ -148,6 +148,15 @@ def test_expert_gemm_host_checks():
     assert L.ep_expert_gemm(ctypes.byref(p), ctypes.byref(lay), fake, 7172, fake, 2048, fake, 0, None) == _lib.EP_EINVAL
     # misaligned base
     assert L.ep_expert_gemm(ctypes.byref(p), ctypes.byref(lay), ctypes.c_void_p((1 << 20) + 8), 0, fake, 2048, fake, 0, None) == _lib.EP_EINVAL
+    # gathered rows need the layout's expert-row map, long enough for every row
+    pg = _lib.Problem(1 << 20, 7168, 8, 1024, 0, 0, _lib.EP_FLAG_GATHER_ROWS)
+    assert L.ep_expert_gemm(ctypes.byref(pg), ctypes.byref(lay), fake, 0, fake, 2048, fake, 0, None) == _lib.EP_EINVAL
+    lay.expert_row_src = 256
+    lay.expert_row_capacity = 100
+    assert L.ep_expert_gemm(ctypes.byref(pg), ctypes.byref(lay), fake, 0, fake, 2048, fake, 0, None) == _lib.EP_EINVAL
+    # unknown flag bits
+    pu = _lib.Problem(16, 7168, 8, 256, 0, 0, 4)
+    assert L.ep_expert_gemm(ctypes.byref(pu), ctypes.byref(lay), fake, 0, fake, 2048, fake, 0, None) == _lib.EP_EINVAL
 
 
 def test_binding_rejects_host_tensors():

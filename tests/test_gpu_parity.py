@@ -338,6 +338,33 @@ def test_dispatch_repeat_bit_identical():
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
 
 
+def test_step_repeat_1000_bit_identical():
+    """The whole step (layout, fp8 dispatch, combine) run 1000 times back to
+    back on one stream: every run's slots, receive bytes and combine output
+    equal the first run's (mismatches are counted on the device and checked
+    once at the end)."""
+    w = W.by_name("mid").replace(mask_p=0.05)
+    idx, wt = W.make_routing(w)
+    d_idx, d_wt = idx.to(DEV), wt.to(DEV)
+    x = W.make_x(w).to(DEV)
+    y = W.make_y(w).to(DEV)
+    L = ep().ep_layout(d_idx, w.E)
+    recv = ep().ep_dispatch(x, L, fp8=True)
+    out = ep().ep_combine(y, L, d_wt)
+    torch.cuda.synchronize()
+    slot0, recv0, out0 = L.slot.clone(), recv.clone(), out.clone()
+    n = L.num_rows()
+    bad = torch.zeros((), dtype=torch.int64, device=DEV)
+    for _ in range(1000):
+        ep().ep_layout(d_idx, w.E, out=L)
+        ep().ep_dispatch(x, L, fp8=True, out=recv)
+        ep().ep_combine(y, L, d_wt, out=out)
+        bad += (L.slot != slot0).sum() + (recv[:n] != recv0[:n]).sum()
+        bad += (out.view(torch.int16) != out0.view(torch.int16)).sum()
+    torch.cuda.synchronize()
+    assert int(bad.item()) == 0
+
+
 # --------------------------------------------------------------------------- combine
 def _combine_case(w, y=None, grouped=False, G=0):
     idx, wt = W.make_routing(w)

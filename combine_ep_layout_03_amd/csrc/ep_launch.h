@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "ep_device.h"
 
@@ -26,11 +27,24 @@ inline int device_cus() {
   return cached[dev];
 }
 
+// EP_MI355X_GRID_BLOCKS=<n> (1 <= n <= 2^20) in the environment replaces the
+// persistent grid size.  The work split gives identical results at any grid
+// size (waves beyond the work return at once), so the override serves grid
+// sweeps in tests and launch tuning; it is read at every launch.
+inline int64_t grid_override() {
+  const char* s = getenv("EP_MI355X_GRID_BLOCKS");
+  if (!s || !*s) return 0;
+  const long long v = atoll(s);
+  return v >= 1 && v <= (1LL << 20) ? v : 0;
+}
+
 // Blocks for a persistent launch of `Kern`: every block the device can keep
 // resident at once, but no more blocks than needed to give each wave one of
 // `items` work items.  Residency is queried once per kernel.
 template <auto Kern>
 inline unsigned persistent_blocks(int64_t items, size_t lds = 0) {
+  const int64_t forced = grid_override();
+  if (forced > 0) return static_cast<unsigned>(forced);
   static int occ = 0;
   if (occ == 0) {
     int n = 0;

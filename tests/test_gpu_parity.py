@@ -508,3 +508,40 @@ def test_round_trip_dispatch_then_unit_weight_combine(mask_p):
     assert exact.any()
     scaled = O.bf16_rne((O.bf16_to_f32(xs[exact]) * k_eff[exact, None]).astype(np.float32))
     assert np.array_equal(got[exact], scaled)
+
+
+@pytest.mark.parametrize("blocks", [1, 3, 64, 5000])
+def test_grid_size_sweep_identical_bytes(blocks, monkeypatch):
+    """The persistent kernels' work split gives the same bytes at any grid
+    size: one block doing everything, a few blocks, and far more blocks than
+    work items (most waves then have nothing to do).  bf16 and fp8 dispatch
+    (both store paths) and flat and grouped combine against the default
+    grid."""
+    w = W.by_name("mid").replace(T=1500, mask_p=0.1, E=64, G=8)
+    idx, wt = W.make_routing(w)
+    d_idx, d_wt = idx.to(DEV), wt.to(DEV)
+    x = W.make_x(w).to(DEV)
+    y = W.make_y(w).to(DEV)
+    L = ep().ep_layout(d_idx, w.E, w.G, d_wt)
+    pitch = ep().fp8_row_pitch(w.H)
+
+    def run():
+        outs = [
+            ep().ep_dispatch(x, L).view(torch.int16),
+            ep().ep_dispatch(x, L, fp8=True),
+            ep().ep_dispatch(x, L, fp8=True, row_stride=pitch),
+            ep().ep_dispatch(x, L, rows=ep().EP_ROWS_GROUP).view(torch.int16),
+            ep().ep_combine(y, L, d_wt).view(torch.int16),
+            ep().ep_combine(y, L, d_wt, d_idx, order=ep().EP_COMBINE_GROUPED).view(torch.int16),
+        ]
+        torch.cuda.synchronize()
+        return outs
+
+    ref = run()
+    n, R = L.num_rows(), L.num_rows(ep().EP_ROWS_GROUP)
+    monkeypatch.setenv("EP_MI355X_GRID_BLOCKS", str(blocks))
+    got = run()
+    monkeypatch.delenv("EP_MI355X_GRID_BLOCKS")
+    rows = [n, n, n, R, w.T, w.T]
+    for a, b, r in zip(ref, got, rows):
+        assert torch.equal(a[:r], b[:r])

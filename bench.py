@@ -12,6 +12,7 @@ Per-op times come from HIP events recorded on the stream the kernels run on
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import platform
@@ -319,6 +320,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="pages")
+    ap.add_argument("--seed", type=int, default=None, help="override the workload's seed")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
     ap.add_argument("--bf16-dispatch", action="store_true", help="also time the bf16 dispatch variant")
@@ -377,6 +379,8 @@ def main(argv=None):
         return 1
     dev = torch.device("cuda:0")
     w = W.by_name(args.workload)
+    if args.seed is not None:
+        w = w.replace(seed=args.seed)
     T, H, K, E = w.T, w.H, w.K, w.E
     print(f"# workload {w.name}: T={T} H={H} K={K} E={E}; generating inputs", file=sys.stderr, flush=True)
     idx, wt = W.make_routing(w)
@@ -386,6 +390,10 @@ def main(argv=None):
     rb = ep.ep_fp8_row_bytes(H)
     pitch = ep.fp8_row_pitch(H)  # 128-byte aligned receive-row pitch (7424 at H=7168)
 
+    inputs_sha256 = {
+        name: hashlib.sha256(t.contiguous().cpu().view(torch.uint8).numpy().tobytes()).hexdigest()[:16]
+        for name, t in (("topk_idx", idx), ("topk_weights", wt), ("x", x), ("y", y))
+    }
     L = ep.ep_layout(d_idx, E)
     n_sel = L.num_rows()
     recv8 = torch.empty(T * K, pitch, dtype=torch.uint8, device=dev)
@@ -586,6 +594,7 @@ def main(argv=None):
             "seq_len": 1,
             "parallelism": "single-GPU",
         },
+        "inputs": {"seed": w.seed, "sha256_16": inputs_sha256},
         "ops": ops,
         "ops_cold_cache": ops_cold,
         "extras": extras,

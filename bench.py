@@ -288,9 +288,22 @@ def cpu_baseline(w, idx, wt, x_host, y_host, sample_tokens):
         "sample": f"full layout of {w.T}x{w.K} ids; fp8 dispatch + combine of the first {S} tokens "
         f"({len(used)} rows); {secs:.1f} s of CPU time; numpy single-threaded elementwise",
         "seconds": {"layout": round(t1 - t0, 3), "dispatch_fp8": round(t3 - t2, 3), "combine": round(t5 - t4, 3)},
-        "cpu_model": platform.processor() or platform.machine(),
+        "cpu_model": host_cpu_model(),
         "host_cpu_count": os.cpu_count(),
+        "affinity_cpus": len(os.sched_getaffinity(0)),
     }
+
+
+def host_cpu_model():
+    """The host CPU's model name from /proc/cpuinfo, else what platform gives."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
 
 
 def smi_snapshot():
@@ -317,8 +330,8 @@ def smi_snapshot():
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="pages")
     ap.add_argument("--seed", type=int, default=None, help="override the workload's seed")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -89,19 +89,57 @@ __device__ __forceinline__ void nt_store(T v, T* p) {
   __builtin_nontemporal_store(v, p);
 }
 
-// Persistent work split: the grid's waves take contiguous, equal (within
-// one item) ranges of `items`.  Returns [begin, end) for the calling wave.
-__device__ __forceinline__ void wave_range(int64_t items, int64_t& begin, int64_t& end) {
-  const int64_t wave = (static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x) / kWave;
-  const int64_t nw = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
-  begin = wave * items / nw;
-  end = (wave + 1) * items / nw;
+// Cyclic work split: wave w of the grid's nw waves takes items w, w + nw,
+// w + 2 nw, ...  At any moment the grid works on a window of about nw
+// consecutive items, so the rows that tokens next to each other read or
+// write (neighbours inside each expert segment) are in flight together.
+// The wave index is read from the first lane so the compiler knows it is
+// wave-uniform: items, tokens and row bases derived from it then live in
+// scalar registers.
+__device__ __forceinline__ int64_t global_wave() {
+  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+  return static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + w;
+}
+__device__ __forceinline__ int64_t grid_waves() {
+  return static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
 }
 
 // Vectors used for row copies (clang extended vectors: one global
 // load/store instruction each).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Raw buffer resource over `bytes` bytes at `p` (byte offsets, no stride;
+// word 3 selects 32-bit data format, as gfx9-family raw loads expect).  A
+// wave-uniform base lives in four scalar registers, so K loads from K rows
+// share one 32-bit vector offset instead of K 64-bit vector addresses.
+// Loads at offsets past `bytes` return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(bytes),
+                                           0x00020000);
+}
+
+// Non-temporal buffer loads of 16, 8, 4 and 2 bytes at byte offset `off`.
+template <typename T>
+__device__ __forceinline__ T buffer_load_nt(__amdgpu_buffer_rsrc_t r, uint32_t off);
+template <>
+__device__ __forceinline__ u32x4 buffer_load_nt<u32x4>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 2);
+}
+template <>
+__device__ __forceinline__ u32x2 buffer_load_nt<u32x2>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, static_cast<int>(off), 0, 2);
+}
+template <>
+__device__ __forceinline__ uint32_t buffer_load_nt<uint32_t>(__amdgpu_buffer_rsrc_t r,
+                                                             uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, 2);
+}
+template <>
+__device__ __forceinline__ uint16_t buffer_load_nt<uint16_t>(__amdgpu_buffer_rsrc_t r,
+                                                             uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(off), 0, 2);
+}
 
 template <int N>
 struct VecOf;

@@ -3,9 +3,8 @@
 // TileScale PR #68 ("EP v2 intranode dispatch/combine") writes every row at
 // send_base[d] + slot, its final compact index, so there is no copy
 // epilogue (PR summary; Design section).  Here a token row is cut into
-// chunks; the persistent grid's waves take contiguous ranges of (token,
-// chunk) items, read each chunk of the source row once and store it once per
-// destination row.  Receive rows are written with non-temporal stores: they
+// chunks; the grid's waves take the (token, chunk) items cyclically, read
+// each chunk of the source row once and store it once per destination row.  Receive rows are written with non-temporal stores: they
 // are not read again by this step and streaming them past the caches
 // measured about 15-20% faster on MI355X than ordinary stores.  Vectors are 16
 // bytes when the row size and base alignment allow, otherwise the widest
@@ -47,21 +46,18 @@ __global__ __launch_bounds__(kBlock) void k_scatter_bf16(ScatterArgs a, int nchu
   using V = typename VecOf<VB>::type;
   if (static_cast<int64_t>(*a.rows_needed) > a.capacity) return;  // overflow: write nothing
   const int lane = threadIdx.x & (kWave - 1);
-  int64_t it, end;
-  wave_range(items, it, end);
-  if (it >= end) return;
-  int64_t t = it / nchunks;
-  int c = static_cast<int>(it - t * nchunks);
+  const int64_t nw = grid_waves();
   const int64_t row_bytes = static_cast<int64_t>(a.H) * 2;
   const int nvec = static_cast<int>(row_bytes / VB);
   char* rbase = static_cast<char*>(a.recv);
   int d[KMAX];
-  load_dests<KMAX>(a, t, lane, d);
-  for (; it < end; ++it, ++c) {
-    if (c == nchunks) {
-      c = 0;
-      ++t;
+  int64_t loaded = -1;
+  for (int64_t it = global_wave(); it < items; it += nw) {
+    const int64_t t = it / nchunks;
+    const int c = static_cast<int>(it - t * nchunks);
+    if (t != loaded) {
       load_dests<KMAX>(a, t, lane, d);
+      loaded = t;
     }
     const V* src = reinterpret_cast<const V*>(static_cast<const char*>(a.x) + t * row_bytes);
     const int vb = c * (kWave * U);
@@ -88,11 +84,12 @@ __global__ __launch_bounds__(kBlock) void k_scatter_bf16(ScatterArgs a, int nchu
 //   a_j = max |x| (exact), s_j = a_j / 448 (IEEE fp32 division),
 //   q = E4M3FN_rne_sat(x / s_j) (IEEE fp32 division), or q = 0 when s_j == 0;
 // bytes: q[0..H) | s_0 .. s_{H/128-1} (fp32, little-endian) | zeros to row_bytes.
-// A wave owns whole tokens.  Each lane converts 16 consecutive elements per
-// step, so 8 lanes form one group and a step covers 1024 elements
-// (H % 128 == 0 keeps every group's 8 lanes together and active).  A step's
-// source elements are loaded one step ahead (the next token's first step
-// during the last step of a token), so the loads fly while a step converts.
+// A wave owns whole tokens, taken cyclically.  Each lane converts 16
+// consecutive elements per step, so 8 lanes form one group and a step covers
+// 1024 elements (H % 128 == 0 keeps every group's 8 lanes together and
+// active).  A step's source elements are loaded one step ahead (the first
+// step of the wave's next token during the last step of a token), so the
+// loads fly while a step converts.
 // The group scales stay in registers (group g in lane g % 64, slot g / 64).
 // With ROWBUF (H <= 8192) the token's whole payload stays in registers too,
 // and each destination row is then written in one burst: payload, scales,
@@ -106,9 +103,9 @@ __global__ __launch_bounds__(kBlock) void k_scatter_fp8(ScatterArgs a, int64_t r
   constexpr int kRowSteps = 8;       // ROWBUF: H <= 8 * 1024
   if (static_cast<int64_t>(*a.rows_needed) > a.capacity) return;
   const int lane = threadIdx.x & (kWave - 1);
-  int64_t t, t_end;
-  wave_range(a.T, t, t_end);
-  if (t >= t_end) return;
+  const int64_t nw = grid_waves();
+  int64_t t = global_wave();
+  if (t >= a.T) return;
   const int H = a.H;
   const int ngroups = H / 128;
   const int nsteps = (H + kWave * 16 - 1) / (kWave * 16);
@@ -133,7 +130,7 @@ __global__ __launch_bounds__(kBlock) void k_scatter_fp8(ScatterArgs a, int64_t r
     const u32x4 in0 = act ? nx0 : u32x4{0u, 0u, 0u, 0u};
     const u32x4 in1 = act ? nx1 : u32x4{0u, 0u, 0u, 0u};
     if (c + 1 < nsteps) load_step(tt, c + 1);
-    else if (tt + 1 < t_end) load_step(tt + 1, 0);
+    else if (tt + nw < a.T) load_step(tt + nw, 0);
     float f[16];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -168,7 +165,7 @@ __global__ __launch_bounds__(kBlock) void k_scatter_fp8(ScatterArgs a, int64_t r
     return q;
   };
   load_step(t, 0);
-  for (; t < t_end; ++t) {
+  for (; t < a.T; t += nw) {
     int d[KMAX];
     load_dests<KMAX>(a, t, lane, d);
 #pragma unroll
@@ -260,14 +257,19 @@ hipError_t scatter_bf16_k(const ScatterArgs& a, int vb, hipStream_t s) {
 // at a line-aligned pitch the step-by-step stores keep more waves resident
 // and measured faster (hidden 7168: 126 vs 146 us at the packed 7392-byte
 // pitch, 118 vs 112 us at 7424).
+// One wave per token: at hidden 7168 the resident grid (six blocks per CU)
+// left a third of its waves a second token, 109 us against 108 us.
+template <int KMAX, bool ROWBUF>
+void kern_launch_fp8(const ScatterArgs& a, int64_t row_bytes, hipStream_t s) {
+  k_scatter_fp8<KMAX, ROWBUF><<<wave_per_item_blocks(a.T), kBlock, 0, s>>>(a, row_bytes);
+}
+
 template <int KMAX>
 hipError_t scatter_fp8_k(const ScatterArgs& a, int64_t row_bytes, hipStream_t s) {
   if (a.H <= 8 * kWave * 16 && a.stride % 128 != 0) {
-    constexpr auto kern = k_scatter_fp8<KMAX, true>;
-    kern<<<persistent_blocks<kern>(a.T), kBlock, 0, s>>>(a, row_bytes);
+    kern_launch_fp8<KMAX, true>(a, row_bytes, s);
   } else {
-    constexpr auto kern = k_scatter_fp8<KMAX, false>;
-    kern<<<persistent_blocks<kern>(a.T), kBlock, 0, s>>>(a, row_bytes);
+    kern_launch_fp8<KMAX, false>(a, row_bytes, s);
   }
   return hipGetLastError();
 }

@@ -512,11 +512,12 @@ def test_round_trip_dispatch_then_unit_weight_combine(mask_p):
 
 @pytest.mark.parametrize("blocks", [1, 3, 64, 5000])
 def test_grid_size_sweep_identical_bytes(blocks, monkeypatch):
-    """The persistent kernels' work split gives the same bytes at any grid
-    size: one block doing everything, a few blocks, and far more blocks than
-    work items (most waves then have nothing to do).  bf16 and fp8 dispatch
-    (both store paths) and flat and grouped combine against the default
-    grid."""
+    """The scatter and combine kernels' cyclic work split gives the same
+    bytes at any grid size: one block doing everything, a few blocks (waves
+    then take several items, of one token or of several), and more blocks
+    than the default one wave per item (the extra waves have nothing to do).
+    bf16 and fp8 dispatch (both store paths) and flat and grouped combine
+    against the default grid."""
     w = W.by_name("mid").replace(T=1500, mask_p=0.1, E=64, G=8)
     idx, wt = W.make_routing(w)
     d_idx, d_wt = idx.to(DEV), wt.to(DEV)

@@ -34,7 +34,9 @@
 // operand reads are issued as inline ds_read_b128 with explicit lgkmcnt
 // waits tied to their registers, so the compiler's wait-count pass, which
 // cannot tell the ring stages apart, does not drain every outstanding load
-// before them.  Sub-tiles without a valid row skip their MFMAs.
+// before them.  Sub-tiles without a valid row skip their MFMAs.  The two
+// waves of each SIMD (one per row half) run half a step apart, so one reads
+// its operands from LDS while the other issues MFMAs (see the main loop).
 //
 // Work: tile t of sum_e ceil(counts[e]/320) * ceil(N/256) tiles (per
 // expert, column-tile major, row-tile minor).  Blocks are dealt to the 8
@@ -111,7 +113,8 @@ __global__ __launch_bounds__(kThreads) void k_expert_gemm(GemmArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  // wave-uniform for the compiler too, so branches on it are scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int E = a.E;
 
   // tiles per expert: ceil(count / 320) row tiles x ceil(N / 256) column
@@ -203,44 +206,76 @@ __global__ __launch_bounds__(kThreads) void k_expert_gemm(GemmArgs a) {
   const uint32_t xbase = lds_addr(sX);
   const uint32_t wbase = lds_addr(sW);
   const int nk = a.H / kBK;
-  for (int kt = 0; kt < kStages - 1 && kt < nk; ++kt) issue(kt);
-  for (int kt = 0; kt < nk; ++kt) {
-    // stage kt landed (for this wave), then for every wave; the barrier also
-    // ends all reads of the stage the next issue overwrites
-    wait_vm(nload * min(kStages - 2, nk - 1 - kt));
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (kt + kStages - 1 < nk) issue(kt + kStages - 1);
-    if (live > 0) {
-      const int st = kt % kStages;
-      const uint32_t xs = xbase + static_cast<uint32_t>(st * kXElems * 2);
-      const uint32_t ws = wbase + static_cast<uint32_t>(st * kWElems * 2);
-      u32x4 av[2][2], bv[2][5];
+  // one stage's operands: 2 reduction halves x (2 weight, 5 receive-row) vectors
+  u32x4 av[2][2], bv[2][5];
+  auto read_stage = [&](int kt) __attribute__((always_inline)) {
+    const int st = kt % kStages;
+    const uint32_t xs = xbase + static_cast<uint32_t>(st * kXElems * 2);
+    const uint32_t ws = wbase + static_cast<uint32_t>(st * kWElems * 2);
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-          av[kk][t] = lds_read16(ws + slot_of(wn * 64 + t * 32 + lr, kk * 2 + lkv) * 16);
+      for (int t = 0; t < 2; ++t)
+        av[kk][t] = lds_read16(ws + slot_of(wn * 64 + t * 32 + lr, kk * 2 + lkv) * 16);
 #pragma unroll
-        for (int i = 0; i < 5; ++i)
-          bv[kk][i] = lds_read16(xs + slot_of((2 * i + wm) * 32 + lr, kk * 2 + lkv) * 16);
-      }
+      for (int i = 0; i < 5; ++i)
+        bv[kk][i] = lds_read16(xs + slot_of((2 * i + wm) * 32 + lr, kk * 2 + lkv) * 16);
+    }
+    lgkm_wait<7>(av[0][0], av[0][1], bv[0][0], bv[0][1], bv[0][2], bv[0][3], bv[0][4]);
+    lgkm_wait<0>(av[1][0], av[1][1], bv[1][0], bv[1][1], bv[1][2], bv[1][3], bv[1][4]);
+  };
+  auto mfma_stage = [&]() __attribute__((always_inline)) {
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        if (kk == 0) lgkm_wait<7>(av[0][0], av[0][1], bv[0][0], bv[0][1], bv[0][2], bv[0][3], bv[0][4]);
-        else lgkm_wait<0>(av[1][0], av[1][1], bv[1][0], bv[1][1], bv[1][2], bv[1][3], bv[1][4]);
+    for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
-        for (int i = 0; i < 5; ++i) {
-          if (i < live) {
+      for (int i = 0; i < 5; ++i) {
+        if (i < live) {
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
-              acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                  as_bf16x8(av[kk][t]), as_bf16x8(bv[kk][i]), acc[i][t], 0, 0, 0);
-          }
+          for (int t = 0; t < 2; ++t)
+            acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                as_bf16x8(av[kk][t]), as_bf16x8(bv[kk][i]), acc[i][t], 0, 0, 0);
         }
       }
     }
+  };
+  auto block_sync = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Ping-pong: each SIMD runs one wave of each row half.  A step has two
+  // phases split by barriers; in the first the row-half-0 waves read stage
+  // kt from LDS while the row-half-1 waves run the MFMAs of step kt - 1, in
+  // the second the roles swap, so the LDS reads of one wave overlap the
+  // MFMAs of the other instead of all eight waves doing each in turn.  The
+  // stage the next issue overwrites was read by both halves before the
+  // step's first barrier, and each wave's wait for its own loads of stage kt
+  // before that barrier makes the stage complete for all.
+  // The two halves run separate loops with the same barriers in the same
+  // order.
+  for (int kt = 0; kt < kStages - 1 && kt < nk; ++kt) issue(kt);
+  if (wm == 0) {
+    for (int kt = 0; kt < nk; ++kt) {
+      wait_vm(nload * min(kStages - 2, nk - 1 - kt));
+      block_sync();
+      if (kt + kStages - 1 < nk) issue(kt + kStages - 1);
+      if (live > 0) read_stage(kt);
+      block_sync();
+      if (live > 0) mfma_stage();
+    }
+  } else {
+    for (int kt = 0; kt < nk; ++kt) {
+      wait_vm(nload * min(kStages - 2, nk - 1 - kt));
+      block_sync();
+      if (kt + kStages - 1 < nk) issue(kt + kStages - 1);
+      if (kt > 0 && live > 0) mfma_stage();
+      block_sync();
+      if (live > 0) read_stage(kt);
+    }
+    if (live > 0) mfma_stage();
   }
 
   // D[n][m] of each 32 x 32 tile: lane -> receive row m = lane % 32, outputs

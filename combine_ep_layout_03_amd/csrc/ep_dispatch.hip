@@ -234,7 +234,7 @@ template <int KMAX, int VB>
 hipError_t scatter_bf16_v(const ScatterArgs& a, hipStream_t s) {
   // One vector per lane per chunk and one wave per chunk: at hidden 7168,
   // top-8 of 256 this measured 185 us against 188 us for four vectors per
-  // lane on the resident grid (and 1146 against 1170 us for the 65,536-token
+  // lane on the resident grid (and 1100 against 1170 us for the 65,536-token
   // grouped rows).
   constexpr int U = 1;
   const int nvec = static_cast<int>(static_cast<int64_t>(a.H) * 2 / VB);

@@ -64,8 +64,9 @@ def time_extras(ep, W, w, d_idx, d_wt, x, y, L, n_sel, rb, pitch, reps, only=Non
     grouped-order combine over 8 groups of 32 experts, the grouped (deduped)
     fp8 dispatch, dispatch into 128-row-aligned expert segments with zeroed
     padding, combine seeded by two bias rows, and the layout with
-    receive-stats accumulation, and the grouped GEMM consumer.  ``only``, if
-    given, names the cases to run."""
+    receive-stats accumulation, the grouped GEMM consumer, the skewed and
+    masked routing, and one GPU's grouped receive share at 65,536 tokens.
+    ``only``, if given, names the cases to run."""
     import torch
 
     dev = x.device
@@ -189,11 +190,66 @@ def time_extras(ep, W, w, d_idx, d_wt, x, y, L, n_sel, rb, pitch, reps, only=Non
         del wts, yg
     if want("grouped_t65536_g8"):
         res["grouped_t65536_g8"] = time_grouped_receive_share(ep, W, dev, stream, gemm_reps)
+    if want("skewed_masked"):
+        res["skewed_masked"] = time_skewed_masked(ep, W, x, y, dev, stream, reps)
     res["_note"] = (
         f"grouped rows R={R} ({R / T:.3f} per token); aligned expert rows {n_al} "
         f"(of which {n_al - n_sel} padding, counted as written bytes)"
     )
     ep.ep_layout(d_idx, E, out=L)  # restore the headline layout
+    return res
+
+
+def time_skewed_masked(ep, W, x, y, dev, stream, reps):
+    """The skewed, masked routing at the bench shape (8192 x 7168, top-8 of
+    256): expert popularity Zipf(1.2) over a seeded permutation, each
+    selection masked with probability 0.1 and 1% of the tokens fully masked.
+    Times its layout, bf16 dispatch and combine on the bench's x and y rows;
+    a fully masked token's row is not read, so dispatch counts the active
+    tokens' rows."""
+    import torch
+
+    w = W.by_name("skewed_masked")
+    T, H, K, E = w.T, w.H, w.K, w.E
+    si, sw = W.make_routing(w)
+    active = int((si >= 0).any(dim=1).sum())
+    si, sw = si.to(dev), sw.to(dev)
+    Ls = ep.ep_layout(si, E)
+    n_sel = Ls.num_rows()
+    counts = Ls.counts.cpu()
+    recv = torch.empty(n_sel, H, dtype=torch.bfloat16, device=dev)
+    out = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    nb = algorithmic_bytes(T, H, K, E, n_sel, 0)
+    cases = {
+        "layout": (lambda: ep.ep_layout(si, E, out=Ls), nb["layout"]),
+        "dispatch_bf16": (
+            lambda: ep.ep_dispatch(x, Ls, out=recv, capacity=n_sel),
+            active * H * 2 + T * K * 4 + n_sel * H * 2,
+        ),
+        "combine": (lambda: ep.ep_combine(y, Ls, sw, out=out), nb["combine"]),
+    }
+    res = {
+        "selections": int(n_sel),
+        "active_tokens": active,
+        "rows_per_expert": {"max": int(counts.max()), "median": int(counts.median()), "min": int(counts.min())},
+    }
+    for name, (fn, nbytes) in cases.items():
+        fn()
+        a0 = torch.cuda.Event(enable_timing=True)
+        a1 = torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        for _ in range(reps):
+            fn()
+        a1.record(stream)
+        torch.cuda.synchronize()
+        us = a0.elapsed_time(a1) * 1e3 / reps
+        res[name] = {
+            "us": round(us, 2),
+            "bytes": int(nbytes),
+            "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "pct_of_peak": round(100.0 * nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
+        }
+    del recv, out, Ls
     return res
 
 

@@ -40,6 +40,16 @@ __device__ __forceinline__ void load_dests(const ScatterArgs& a, int64_t t, int 
   }
 }
 
+// Has the token any destination row?  (Wave-uniform: d is.)  A token
+// without one is not read at all.
+template <int KMAX>
+__device__ __forceinline__ bool any_dest(const int (&d)[KMAX]) {
+  bool any = false;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) any = any || d[j] >= 0;
+  return any;
+}
+
 template <int KMAX, int VB, int U>
 __global__ __launch_bounds__(kBlock) void k_scatter_bf16(ScatterArgs a, int nchunks,
                                                          int64_t items) {
@@ -52,13 +62,16 @@ __global__ __launch_bounds__(kBlock) void k_scatter_bf16(ScatterArgs a, int nchu
   char* rbase = static_cast<char*>(a.recv);
   int d[KMAX];
   int64_t loaded = -1;
+  bool any = false;
   for (int64_t it = global_wave(); it < items; it += nw) {
     const int64_t t = it / nchunks;
     const int c = static_cast<int>(it - t * nchunks);
     if (t != loaded) {
       load_dests<KMAX>(a, t, lane, d);
+      any = any_dest<KMAX>(d);
       loaded = t;
     }
+    if (!any) continue;
     const V* src = reinterpret_cast<const V*>(static_cast<const char*>(a.x) + t * row_bytes);
     const int vb = c * (kWave * U);
     V val[U];
@@ -89,7 +102,8 @@ __global__ __launch_bounds__(kBlock) void k_scatter_bf16(ScatterArgs a, int nchu
 // 1024 elements (H % 128 == 0 keeps every group's 8 lanes together and
 // active).  A step's source elements are loaded one step ahead (the first
 // step of the wave's next token during the last step of a token), so the
-// loads fly while a step converts.
+// loads fly while a step converts.  A token without a destination row is
+// skipped unread.
 // The group scales stay in registers (group g in lane g % 64, slot g / 64).
 // With ROWBUF (H <= 8192) the token's whole payload stays in registers too,
 // and each destination row is then written in one burst: payload, scales,
@@ -164,10 +178,15 @@ __global__ __launch_bounds__(kBlock) void k_scatter_fp8(ScatterArgs a, int64_t r
       if (keep && r == (c >> 3)) my_sc[r] = sc;
     return q;
   };
-  load_step(t, 0);
+  bool have0 = false;  // step 0 of token t is loaded (by the previous token's last step)
   for (; t < a.T; t += nw) {
     int d[KMAX];
     load_dests<KMAX>(a, t, lane, d);
+    if (!any_dest<KMAX>(d)) {
+      have0 = false;
+      continue;
+    }
+    if (!have0) load_step(t, 0);
 #pragma unroll
     for (int r = 0; r < kMaxScaleSlots; ++r) my_sc[r] = 0.0f;
     u32x4 qrow[ROWBUF ? kRowSteps : 1];
@@ -206,6 +225,7 @@ __global__ __launch_bounds__(kBlock) void k_scatter_fp8(ScatterArgs a, int64_t r
       // zero padding after the scales (a multiple of 4 bytes, under 16)
       if (lane < pad_words) nt_store(0u, reinterpret_cast<uint32_t*>(tail + 4 * ngroups) + lane);
     }
+    have0 = t + nw < a.T;  // the last step loaded the next token's step 0
   }
 }
 

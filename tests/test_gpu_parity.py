@@ -517,8 +517,11 @@ def test_grid_size_sweep_identical_bytes(blocks, monkeypatch):
     then take several items, of one token or of several), and more blocks
     than the default one wave per item (the extra waves have nothing to do).
     bf16 and fp8 dispatch (both store paths) and flat and grouped combine
-    against the default grid."""
-    w = W.by_name("mid").replace(T=1500, mask_p=0.1, E=64, G=8)
+    against the default grid.  5% of the tokens are fully masked, so waves
+    that walk several tokens step over tokens they must not read; the
+    default grid's fp8 rows are checked against the oracle too."""
+    say("grid sweep", blocks)
+    w = W.by_name("mid").replace(T=1500, mask_p=0.1, full_mask_frac=0.05, E=64, G=8)
     idx, wt = W.make_routing(w)
     d_idx, d_wt = idx.to(DEV), wt.to(DEV)
     x = W.make_x(w).to(DEV)
@@ -540,6 +543,9 @@ def test_grid_size_sweep_identical_bytes(blocks, monkeypatch):
 
     ref = run()
     n, R = L.num_rows(), L.num_rows(ep().EP_ROWS_GROUP)
+    assert (idx.numpy() < 0).all(axis=1).sum() >= round(0.05 * w.T)
+    want = O.dispatch_fp8(u16(x), O.layout(idx.numpy(), w.E)["slot"], n)
+    assert np.array_equal(ref[1][:n].cpu().numpy(), want)
     monkeypatch.setenv("EP_MI355X_GRID_BLOCKS", str(blocks))
     got = run()
     monkeypatch.delenv("EP_MI355X_GRID_BLOCKS")

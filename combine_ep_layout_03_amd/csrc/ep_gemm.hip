@@ -11,14 +11,18 @@
 // Tiling for gfx950: a 512-thread block computes up to 320 rows x 256
 // columns of one expert, so an expert of up to 320 receive rows (all of them
 // at the 8192-token, top-8-of-256 shape) streams each weight slice through
-// one CU only.  The reduction runs 32 at a time through a 4-stage LDS ring
-// (144 KiB) filled by LDS-direct loads (global_load_lds_dwordx4: each lane's
-// 16 bytes land in LDS without passing through registers), issued three
-// steps ahead.  A stage holds the tile's rows of 4 16-byte k-vectors per
-// operand; vector kv of row r sits in slot r*4 + (kv ^ ((r >> 2) & 3)), which
-// keeps the 16-byte operand reads of 16 consecutive rows on distinct banks.
-// Waves 0-3 fill the receive-row stage (5 KiB each), waves 4-7 the weight
-// stage (4 KiB each).
+// one CU only.  The reduction runs 32 at a time (one step) through two LDS
+// rings (144 KiB) filled by LDS-direct loads (global_load_lds_dwordx4: each
+// lane's 16 bytes land in LDS without passing through registers).  Weight
+// stages are one step wide, 4 of them, issued three steps ahead.
+// Receive-row stages are two steps wide, 2 of them, one stage ahead: a
+// receive row's 64 elements of a stage are one whole 128-byte line, which the
+// 8 column tiles of an expert read from L2 (whole lines measured 1.5% faster
+// than half lines).  Vector kv of row r sits in slot r*4 + (kv ^ ((r >> 2) &
+// 3)) of a weight stage and r*8 + (kv ^ ((r >> 1) & 7)) of a receive-row
+// stage, which keeps the 16-byte operand reads of 16 consecutive rows on
+// distinct banks.  Waves 0-3 fill the receive-row stage (10 KiB each), waves
+// 4-7 the weight stage (4 KiB each).
 //
 // The 8 waves form 2 (rows) x 4 (columns).  A wave owns 64 columns and the
 // 32-row sub-tiles wm, wm+2, ..., wm+8 (interleaved, so a tile of any height
@@ -30,7 +34,7 @@
 // Every lane loads a full stage share (rows past the tile, or past N,
 // re-read a valid row and are never stored), which keeps the number of
 // loads in flight per wave exact: waiting until at most (loads per stage) *
-// (stages still ahead) remain marks the current stage complete.  The LDS
+// (younger stages issued) remain marks the stage a step reads complete.  The LDS
 // operand reads are issued as inline ds_read_b128 with explicit lgkmcnt
 // waits tied to their registers, so the compiler's wait-count pass, which
 // cannot tell the ring stages apart, does not drain every outstanding load
@@ -61,15 +65,20 @@ constexpr int kThreads = 512;   // 8 waves: 2 (rows) x 4 (columns)
 constexpr int kBM = 320;        // receive rows per tile (at most)
 constexpr int kBN = 256;        // output columns per tile
 constexpr int kBK = 32;         // reduction step
-constexpr int kStages = 4;      // LDS ring depth
-constexpr int kXElems = kBM * kBK;  // bf16 elements of a receive-row stage (20 KiB)
-constexpr int kWElems = kBN * kBK;  // bf16 elements of a weight stage (16 KiB)
+constexpr int kXStages = 2;     // receive-row ring: 64-wide stages (whole 128-B lines), one ahead
+constexpr int kWStages = 4;     // weight ring: 32-wide stages, three ahead
+constexpr int kXBK = 2 * kBK;   // reduction width of a receive-row stage
+constexpr int kXElems = kBM * kXBK;  // bf16 elements of a receive-row stage (40 KiB)
+constexpr int kWElems = kBN * kBK;   // bf16 elements of a weight stage (16 KiB)
 constexpr int kXcds = 8;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// 16-byte slot of k-vector kv (0..3) of row r within a stage
-__device__ __forceinline__ int slot_of(int r, int kv) { return r * 4 + (kv ^ ((r >> 2) & 3)); }
+// 16-byte slot of k-vector kv of row r within a weight stage (kv 0..3) or a
+// receive-row stage (kv 0..7); the XOR keeps the operand reads of 16
+// consecutive rows at one kv on distinct banks
+__device__ __forceinline__ int slot_w(int r, int kv) { return r * 4 + (kv ^ ((r >> 2) & 3)); }
+__device__ __forceinline__ int slot_x(int r, int kv) { return r * 8 + (kv ^ ((r >> 1) & 7)); }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(
@@ -93,19 +102,18 @@ __device__ __forceinline__ void lgkm_wait(u32x4& a0, u32x4& a1, u32x4& b0, u32x4
                : "n"(N));
 }
 
-// wait until at most n (0, 4, 5, 8 or 10) vector-memory loads of this wave
-// are outstanding; expcnt and lgkmcnt are left unconstrained
+// wait until at most n (0, 4, 8 or 10) vector-memory loads of this wave are
+// outstanding; expcnt and lgkmcnt are left unconstrained
 __device__ __forceinline__ void wait_vm(int n) {
   if (n >= 10) __builtin_amdgcn_s_waitcnt(0xF70 | 10);
   else if (n >= 8) __builtin_amdgcn_s_waitcnt(0xF70 | 8);
-  else if (n >= 5) __builtin_amdgcn_s_waitcnt(0xF70 | 5);
   else if (n >= 4) __builtin_amdgcn_s_waitcnt(0xF70 | 4);
   else __builtin_amdgcn_s_waitcnt(0xF70);
 }
 
 __global__ __launch_bounds__(kThreads) void k_expert_gemm(GemmArgs a) {
-  __shared__ __align__(16) uint16_t sX[kStages * kXElems];
-  __shared__ __align__(16) uint16_t sW[kStages * kWElems];
+  __shared__ __align__(16) uint16_t sX[kXStages * kXElems];
+  __shared__ __align__(16) uint16_t sW[kWStages * kWElems];
   // tile table (E + 1 ints) and scan scratch, in the ring until the first load
   static_assert((1024 + 1 + 16 + kThreads / kWave) * sizeof(int) <= sizeof(sW), "tile table fits");
   int* const sTiles = reinterpret_cast<int*>(sW);
@@ -150,40 +158,78 @@ __global__ __launch_bounds__(kThreads) void k_expert_gemm(GemmArgs a) {
   const int n0 = jn * kBN;
   __syncthreads();  // every read of the tile table precedes the ring's first load
 
-  // Waves 0-3 fill the receive-row stage (20 chunks of 64 slots, 5 each),
-  // waves 4-7 the weight stage (16 chunks, 4 each): lane l of chunk j fills
-  // slot s = j*64 + l, i.e. row s/4, k-vector (s % 4) ^ ((row >> 2) & 3).
+  // Waves 0-3 fill the receive-row stage (40 chunks of 64 slots, 10 each):
+  // lane l of chunk j fills slot s = j*64 + l, row s/8, k-vector
+  // (s % 8) ^ ((row >> 1) & 7), so one load instruction covers 8 whole
+  // 128-byte lines of 8 receive rows.  Waves 4-7 fill the weight stage (16
+  // chunks, 4 each): row s/4, k-vector (s % 4) ^ ((row >> 2) & 3).
   const bool xwave = wave < 4;
-  const int nload = xwave ? 5 : 4;
-  const uint16_t* src[5];
-  int dst[5];
+  const uint16_t* src[10];
+  int dst[10];
 #pragma unroll
-  for (int q = 0; q < 5; ++q) {
-    const int j = xwave ? wave * 5 + q : (wave - 4) * 4 + (q < 4 ? q : 3);
-    const int s = j * 64 + lane;
-    const int r = s >> 2;
-    const int kv = (s & 3) ^ ((r >> 2) & 3);
+  for (int q = 0; q < 10; ++q) {
     if (xwave) {
+      const int j = wave * 10 + q;
+      const int s = j * 64 + lane;
+      const int r = s >> 3;
+      const int kv = (s & 7) ^ ((r >> 1) & 7);
       const int xr = r < nrows ? r : 0;
       // expert row -> the x row holding its operand: itself, or (rows
       // gathered) the token it came from
       const int64_t xrow = a.row_src ? a.row_src[row0 + xr] : row0 + xr;
       src[q] = a.x + xrow * a.ldx + kv * 8;
+      dst[q] = j * 64 * 8;
     } else {
+      const int j = (wave - 4) * 4 + (q < 4 ? q : 3);
+      const int s = j * 64 + lane;
+      const int r = s >> 2;
+      const int kv = (s & 3) ^ ((r >> 2) & 3);
       const int wr = n0 + r < a.N ? r : 0;  // the last column tile may be half valid
       src[q] = a.w + (static_cast<int64_t>(e) * a.N + n0 + wr) * a.H + kv * 8;
+      dst[q] = j * 64 * 8;
     }
-    dst[q] = j * 64 * 8;
   }
-  auto issue = [&](int kt) {
-    const int st = kt % kStages;
-    uint16_t* base = xwave ? sX + st * kXElems : sW + st * kWElems;
+  const int nk = a.H / kBK;  // 32-wide steps; H % 64 == 0, so nk is even
+  const int nsx = nk / 2;    // receive-row stages
+  auto issue_x = [&](int sx) __attribute__((always_inline)) {
+    uint16_t* base = sX + (sx % kXStages) * kXElems;
 #pragma unroll
-    for (int q = 0; q < 5; ++q) {
-      if (q < nload)
-        __builtin_amdgcn_global_load_lds(
-            (const __attribute__((address_space(1))) void*)(src[q] + kt * kBK),
-            (__attribute__((address_space(3))) void*)(base + dst[q]), 16, 0, 0);
+    for (int q = 0; q < 10; ++q)
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(src[q] + sx * kXBK),
+          (__attribute__((address_space(3))) void*)(base + dst[q]), 16, 0, 0);
+  };
+  auto issue_w = [&](int kt) __attribute__((always_inline)) {
+    uint16_t* base = sW + (kt % kWStages) * kWElems;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(src[q] + kt * kBK),
+          (__attribute__((address_space(3))) void*)(base + dst[q]), 16, 0, 0);
+  };
+  // this wave's loads of the stages step kt reads have landed.  Receive-row
+  // stage kt/2: stages 0 and 1 are issued up front and stage s + 1 at step
+  // 2s (s >= 1), so before even steps only stage 1 at step 0 is younger, and
+  // before odd steps stage kt/2 + 1 (10 loads each).  Weight stage kt:
+  // stages kt + 1 and kt + 2 are younger (4 loads each).
+  auto wait_own = [&](int kt) __attribute__((always_inline)) {
+    if (xwave) {
+      const int sx = kt >> 1;
+      const int issued = min(nsx - 1, (kt & 1) ? sx + 1 : max(sx, 1));
+      wait_vm(10 * (issued - sx));
+    } else {
+      wait_vm(4 * min(kWStages - 2, nk - 1 - kt));
+    }
+  };
+  // after step kt's first barrier: on even steps kt = 2s >= 2 receive-row
+  // stage s + 1 (its slot held stage s - 1), and weight stage kt + 3 (its
+  // slot held stage kt - 1); both were read by both halves before that
+  // barrier
+  auto issue_next = [&](int kt) __attribute__((always_inline)) {
+    if (xwave) {
+      if (!(kt & 1) && kt >= 2 && (kt >> 1) + 1 < nsx) issue_x((kt >> 1) + 1);
+    } else if (kt + kWStages - 1 < nk) {
+      issue_w(kt + kWStages - 1);
     }
   };
 
@@ -205,21 +251,20 @@ __global__ __launch_bounds__(kThreads) void k_expert_gemm(GemmArgs a) {
 
   const uint32_t xbase = lds_addr(sX);
   const uint32_t wbase = lds_addr(sW);
-  const int nk = a.H / kBK;
   // one stage's operands: 2 reduction halves x (2 weight, 5 receive-row) vectors
   u32x4 av[2][2], bv[2][5];
   auto read_stage = [&](int kt) __attribute__((always_inline)) {
-    const int st = kt % kStages;
-    const uint32_t xs = xbase + static_cast<uint32_t>(st * kXElems * 2);
-    const uint32_t ws = wbase + static_cast<uint32_t>(st * kWElems * 2);
+    const uint32_t xs = xbase + static_cast<uint32_t>(((kt >> 1) % kXStages) * kXElems * 2);
+    const uint32_t ws = wbase + static_cast<uint32_t>((kt % kWStages) * kWElems * 2);
+    const int xk = (kt & 1) * 4;  // this step's k-vectors inside the receive-row stage
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
       for (int t = 0; t < 2; ++t)
-        av[kk][t] = lds_read16(ws + slot_of(wn * 64 + t * 32 + lr, kk * 2 + lkv) * 16);
+        av[kk][t] = lds_read16(ws + slot_w(wn * 64 + t * 32 + lr, kk * 2 + lkv) * 16);
 #pragma unroll
       for (int i = 0; i < 5; ++i)
-        bv[kk][i] = lds_read16(xs + slot_of((2 * i + wm) * 32 + lr, kk * 2 + lkv) * 16);
+        bv[kk][i] = lds_read16(xs + slot_x((2 * i + wm) * 32 + lr, xk + kk * 2 + lkv) * 16);
     }
     lgkm_wait<7>(av[0][0], av[0][1], bv[0][0], bv[0][1], bv[0][2], bv[0][3], bv[0][4]);
     lgkm_wait<0>(av[1][0], av[1][1], bv[1][0], bv[1][1], bv[1][2], bv[1][3], bv[1][4]);
@@ -256,21 +301,26 @@ __global__ __launch_bounds__(kThreads) void k_expert_gemm(GemmArgs a) {
   // before that barrier makes the stage complete for all.
   // The two halves run separate loops with the same barriers in the same
   // order.
-  for (int kt = 0; kt < kStages - 1 && kt < nk; ++kt) issue(kt);
+  if (xwave) {
+    issue_x(0);
+    if (nsx > 1) issue_x(1);
+  } else {
+    for (int kt = 0; kt < kWStages - 1 && kt < nk; ++kt) issue_w(kt);
+  }
   if (wm == 0) {
     for (int kt = 0; kt < nk; ++kt) {
-      wait_vm(nload * min(kStages - 2, nk - 1 - kt));
+      wait_own(kt);
       block_sync();
-      if (kt + kStages - 1 < nk) issue(kt + kStages - 1);
+      issue_next(kt);
       if (live > 0) read_stage(kt);
       block_sync();
       if (live > 0) mfma_stage();
     }
   } else {
     for (int kt = 0; kt < nk; ++kt) {
-      wait_vm(nload * min(kStages - 2, nk - 1 - kt));
+      wait_own(kt);
       block_sync();
-      if (kt + kStages - 1 < nk) issue(kt + kStages - 1);
+      issue_next(kt);
       if (kt > 0 && live > 0) mfma_stage();
       block_sync();
       if (live > 0) read_stage(kt);

@@ -64,7 +64,8 @@ def time_extras(ep, W, w, d_idx, d_wt, x, y, L, n_sel, rb, pitch, reps, only=Non
     grouped-order combine over 8 groups of 32 experts, the grouped (deduped)
     fp8 dispatch, dispatch into 128-row-aligned expert segments with zeroed
     padding, combine seeded by two bias rows, and the layout with
-    receive-stats accumulation, the grouped GEMM consumer, the skewed and
+    receive-stats accumulation, the grouped GEMM consumer (plain weights,
+    packed weights, and fused with the dispatch), the skewed and
     masked routing, and one GPU's grouped receive share at 65,536 tokens.
     ``only``, if given, names the cases to run."""
     import torch
@@ -146,7 +147,8 @@ def time_extras(ep, W, w, d_idx, d_wt, x, y, L, n_sel, rb, pitch, reps, only=Non
         torch.cuda.synchronize()
         return b0.elapsed_time(b1) * 1e3 / n
 
-    if want("expert_gemm_bf16_n2048") or want("expert_gemm_fused_dispatch_n2048"):
+    gemm_cases = ("expert_gemm_bf16_n2048", "expert_gemm_fused_dispatch_n2048", "expert_gemm_packed_weights_n2048")
+    if any(want(c) for c in gemm_cases):
         wts = W.make_expert_weights(w, N, device=dev)
         yg = torch.empty(L.max_expert_rows(), N, dtype=torch.bfloat16, device=dev)
         if want("expert_gemm_bf16_n2048"):
@@ -164,6 +166,23 @@ def time_extras(ep, W, w, d_idx, d_wt, x, y, L, n_sel, rb, pitch, reps, only=Non
                 "traffic": counted_traffic("expert_gemm_n2048", w.name),
             }
             del xr
+        if want("expert_gemm_packed_weights_n2048"):
+            # weights packed once into the kernel's tile order (outside the
+            # timed region, as static weights are), then the same GEMM
+            xr = W.make_rows(w, L.max_expert_rows(), device=dev)
+            packed = ep.ep_pack_expert_weights(wts)
+            us_p = timed(lambda: ep.ep_expert_gemm(xr, L, packed, out=yg), gemm_reps)
+            us_plain = timed(lambda: ep.ep_expert_gemm(xr, L, wts, out=yg), gemm_reps)
+            nbytes = E * N * H * 2 + n_sel * H * 2 + n_sel * N * 2
+            res["expert_gemm_packed_weights_n2048"] = {
+                "us": round(us_p, 1),
+                "us_plain_weights": round(us_plain, 1),
+                "TFLOPs": round(flops / (us_p * 1e-6) / 1e12, 1),
+                "pct_of_mfma_peak": round(100.0 * flops / (us_p * 1e-6) / 2.5e15, 1),
+                "GBps": round(nbytes / (us_p * 1e-6) / 1e9, 1),
+                "pct_of_hbm_peak": round(100.0 * nbytes / (us_p * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
+            }
+            del xr, packed
         if want("expert_gemm_fused_dispatch_n2048"):
             # the same GEMM with the dispatch folded into its loads (rows
             # gathered from the token matrix through expert_row_src), against

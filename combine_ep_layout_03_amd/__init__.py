@@ -44,6 +44,9 @@ __all__ = [
     "ep_dispatch",
     "ep_combine",
     "ep_expert_gemm",
+    "PackedExpertWeights",
+    "ep_expert_weights_packed_bytes",
+    "ep_pack_expert_weights",
     "ep_strerror",
     "EPError",
 ]
@@ -400,29 +403,74 @@ def ep_combine(
     return out
 
 
+@dataclasses.dataclass(frozen=True)
+class PackedExpertWeights:
+    """Expert weights bf16 [E, N, H] packed once into the grouped GEMM's tile
+    order (``ep_pack_expert_weights``); pass it to ``ep_expert_gemm`` in
+    place of the [E, N, H] tensor."""
+
+    data: torch.Tensor  # bf16, ep_expert_weights_packed_bytes(E, N, H) / 2 elements
+    num_experts: int
+    n_out: int
+    hidden: int
+
+
+def ep_expert_weights_packed_bytes(num_experts: int, n_out: int, hidden: int) -> int:
+    return int(_lib.lib().ep_expert_weights_packed_bytes(int(num_experts), int(n_out), int(hidden)))
+
+
+def ep_pack_expert_weights(w: torch.Tensor) -> PackedExpertWeights:
+    """Pack bf16 [E, N, H] expert weights for ``ep_expert_gemm``: every
+    (expert, 256-column tile, 32-wide reduction step) block becomes 16 KiB
+    contiguous, rows past N zero."""
+    _dev(w, "w", torch.bfloat16)
+    if w.dim() != 3:
+        raise ValueError("w must be [E, N, H]")
+    E, N, H = w.shape
+    nbytes = ep_expert_weights_packed_bytes(E, N, H)
+    if nbytes < 0:
+        raise ValueError("packed weights need N % 128 == 0 and H % 64 == 0")
+    data = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=w.device)
+    rc = _lib.lib().ep_pack_expert_weights(_ptr(w), int(E), int(N), int(H), _ptr(data), _stream(w.device))
+    _lib.check("ep_pack_expert_weights", rc)
+    return PackedExpertWeights(data, int(E), int(N), int(H))
+
+
 def ep_expert_gemm(
     x: torch.Tensor,
     layout: Layout,
-    w: torch.Tensor,
+    w: torch.Tensor | PackedExpertWeights,
     out: torch.Tensor | None = None,
     gather: bool = False,
 ) -> torch.Tensor:
     """Grouped GEMM over the expert-major segments: y[r] = x_r @ w[e]^T for
-    each receive row r of expert e; w: bf16 [E, N, H]; returns y bf16
-    [rows, N] (rows outside the experts' selections are left as they were).
+    each receive row r of expert e; w: bf16 [E, N, H], or those weights
+    packed by ``ep_pack_expert_weights``; returns y bf16 [rows, N] (rows
+    outside the experts' selections are left as they were).
 
     x_r is row r of x (bf16 [rows, >= H], the dispatched receive rows), or,
     with ``gather``, row expert_row_src[r] of the token matrix x (bf16
     [T, >= H]): the dispatch folded into the GEMM's loads, which needs a
     layout computed with ``expert_row_src=True``."""
     layout = _resolve(layout)
-    if x.dim() != 2 or w.dim() != 3:
-        raise ValueError("x must be [rows, H] and w [E, N, H]")
+    packed = isinstance(w, PackedExpertWeights)
+    if packed:
+        E, N, H = w.num_experts, w.n_out, w.hidden
+        _dev(w.data, "w.data", torch.bfloat16)
+        if w.data.numel() * 2 != ep_expert_weights_packed_bytes(E, N, H):
+            raise ValueError("packed weights of the wrong size")
+        wt = w.data
+    else:
+        if w.dim() != 3:
+            raise ValueError("w must be [E, N, H]")
+        E, N, H = w.shape
+        _dev(w, "w", torch.bfloat16)
+        wt = w
+    if x.dim() != 2:
+        raise ValueError("x must be [rows, H]")
     _dev(x, "x", torch.bfloat16)
-    E, N, H = w.shape
     if E != layout.num_experts:
         raise ValueError("w must hold one [N, H] matrix per expert")
-    _dev(w, "w", torch.bfloat16)
     if x.shape[1] < H:
         raise ValueError("x rows are shorter than H")
     rows = layout.max_expert_rows()
@@ -439,12 +487,12 @@ def ep_expert_gemm(
         _dev(out, "out", torch.bfloat16)
         if out.dim() != 2 or out.shape[1] < N or out.shape[0] < rows:
             raise ValueError("out must be bf16 [>= expert rows, >= N]")
-    flags = _lib.EP_FLAG_GATHER_ROWS if gather else 0
+    flags = (_lib.EP_FLAG_GATHER_ROWS if gather else 0) | (_lib.EP_FLAG_PACKED_WEIGHTS if packed else 0)
     p = _problem(layout.num_tokens, H, layout.topk, layout.num_experts, layout.num_groups,
                  layout.expert_alignment, flags)
     s = layout.struct()
     rc = _lib.lib().ep_expert_gemm(
-        ctypes.byref(p), ctypes.byref(s), _ptr(x), int(x.shape[1]), _ptr(w), int(N), _ptr(out), int(out.shape[1]),
+        ctypes.byref(p), ctypes.byref(s), _ptr(x), int(x.shape[1]), _ptr(wt), int(N), _ptr(out), int(out.shape[1]),
         _stream(x.device),
     )
     _lib.check("ep_expert_gemm", rc)

@@ -32,6 +32,7 @@ EP_STATUS_WORDS = 8
 
 EP_FLAG_ZERO_PADDING = 1
 EP_FLAG_GATHER_ROWS = 2
+EP_FLAG_PACKED_WEIGHTS = 4
 
 EP_FORMAT_BF16 = 0
 EP_FORMAT_FP8_PACKED = 1
@@ -47,6 +48,8 @@ EXPORTS = (
     "ep_dispatch",
     "ep_combine",
     "ep_expert_gemm",
+    "ep_expert_weights_packed_bytes",
+    "ep_pack_expert_weights",
     "ep_strerror",
 )
 
@@ -117,6 +120,10 @@ def lib(path: str | None = None) -> ctypes.CDLL:
     L.ep_combine.restype = ctypes.c_int
     L.ep_expert_gemm.argtypes = [P, LS, vp, ctypes.c_int64, vp, ctypes.c_int32, vp, ctypes.c_int64, vp]
     L.ep_expert_gemm.restype = ctypes.c_int
+    L.ep_expert_weights_packed_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+    L.ep_expert_weights_packed_bytes.restype = ctypes.c_int64
+    L.ep_pack_expert_weights.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp]
+    L.ep_pack_expert_weights.restype = ctypes.c_int
     L.ep_strerror.argtypes = [ctypes.c_int]
     L.ep_strerror.restype = ctypes.c_char_p
     if path is None:

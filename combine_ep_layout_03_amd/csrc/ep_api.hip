@@ -18,7 +18,7 @@ int check_problem(const ep_problem_t* p) {
     return EP_EINVAL;
   if (p->num_groups > 0 && p->num_experts % p->num_groups != 0) return EP_EINVAL;
   if (p->expert_alignment < 0 || p->expert_alignment > (1 << 20)) return EP_EINVAL;
-  if (p->flags & ~(EP_FLAG_ZERO_PADDING | EP_FLAG_GATHER_ROWS)) return EP_EINVAL;
+  if (p->flags & ~(EP_FLAG_ZERO_PADDING | EP_FLAG_GATHER_ROWS | EP_FLAG_PACKED_WEIGHTS)) return EP_EINVAL;
   if (p->topk > EP_MAX_TOPK) return EP_ENOTSUP;
   if (static_cast<int64_t>(p->num_experts) + p->num_groups > EP_MAX_KEYS) return EP_ENOTSUP;
   // slots and rows are int32: every (t,k) row, padding included, must index below 2^31
@@ -219,6 +219,7 @@ int ep_expert_gemm(const ep_problem_t* p, const ep_layout_t* L, const void* x,
                       (p->expert_alignment > 1 ? p->expert_alignment - 1 : 0);
   const int64_t max_rows = p->num_tokens * p->topk + pad;
   a.row_src = nullptr;
+  a.packed = (p->flags & EP_FLAG_PACKED_WEIGHTS) != 0;
   if (p->flags & EP_FLAG_GATHER_ROWS) {
     // token rows gathered through the layout's expert-row map, which must
     // cover every expert row the layout can produce
@@ -228,6 +229,21 @@ int ep_expert_gemm(const ep_problem_t* p, const ep_layout_t* L, const void* x,
   // the kernel numbers its tiles in int32
   if (ep::expert_gemm_max_tiles(max_rows, p->num_experts, n_out) > INT32_MAX) return EP_ENOTSUP;
   return ep::launch_expert_gemm(a, max_rows, stream) == hipSuccess ? EP_OK : EP_EHIP;
+}
+
+int64_t ep_expert_weights_packed_bytes(int32_t num_experts, int32_t n_out, int32_t hidden) {
+  if (num_experts < 1 || n_out < 1 || hidden < 1 || n_out % 128 != 0 || hidden % 64 != 0) return -1;
+  return static_cast<int64_t>(num_experts) * ((n_out + 255) / 256) * 256 * hidden * 2;
+}
+
+int ep_pack_expert_weights(const void* w, int32_t num_experts, int32_t n_out, int32_t hidden,
+                           void* w_packed, hipStream_t stream) {
+  if (ep_expert_weights_packed_bytes(num_experts, n_out, hidden) < 0) return EP_EINVAL;
+  if (!w || !w_packed || !aligned(w, 16) || !aligned(w_packed, 16)) return EP_EINVAL;
+  return ep::launch_pack_expert_weights(static_cast<const uint16_t*>(w), num_experts, n_out, hidden,
+                                        static_cast<uint16_t*>(w_packed), stream) == hipSuccess
+             ? EP_OK
+             : EP_EHIP;
 }
 
 const char* ep_strerror(int code) {

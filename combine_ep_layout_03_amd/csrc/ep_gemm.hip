@@ -184,11 +184,20 @@ __global__ __launch_bounds__(kThreads) void k_expert_gemm(GemmArgs a) {
       const int s = j * 64 + lane;
       const int r = s >> 2;
       const int kv = (s & 3) ^ ((r >> 2) & 3);
-      const int wr = n0 + r < a.N ? r : 0;  // the last column tile may be half valid
-      src[q] = a.w + (static_cast<int64_t>(e) * a.N + n0 + wr) * a.H + kv * 8;
+      if (a.packed) {
+        // the (expert, column tile) block; rows past N are zero there
+        src[q] = a.w + (static_cast<int64_t>(e) * a.ntn + jn) * (static_cast<int64_t>(a.H) * kBN) +
+                 r * kBK + kv * 8;
+      } else {
+        const int wr = n0 + r < a.N ? r : 0;  // the last column tile may be half valid
+        src[q] = a.w + (static_cast<int64_t>(e) * a.N + n0 + wr) * a.H + kv * 8;
+      }
       dst[q] = j * 64 * 8;
     }
   }
+  // elements between consecutive weight stages of one row: the next 32 of
+  // the row, or the next 16 KiB block of the packed order
+  const int64_t wstep = a.packed ? kBN * kBK : kBK;
   const int nk = a.H / kBK;  // 32-wide steps; H % 64 == 0, so nk is even
   const int nsx = nk / 2;    // receive-row stages
   auto issue_x = [&](int sx) __attribute__((always_inline)) {
@@ -204,7 +213,7 @@ __global__ __launch_bounds__(kThreads) void k_expert_gemm(GemmArgs a) {
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(src[q] + kt * kBK),
+          (const __attribute__((address_space(1))) void*)(src[q] + kt * wstep),
           (__attribute__((address_space(3))) void*)(base + dst[q]), 16, 0, 0);
   };
   // this wave's loads of the stages step kt reads have landed.  Receive-row
@@ -349,7 +358,39 @@ __global__ __launch_bounds__(kThreads) void k_expert_gemm(GemmArgs a) {
   }
 }
 
+// One 16-byte chunk per thread of the packed order: chunk c is k-vector
+// c % 4 of row (c / 4) % 256 of block c / 1024, block = (expert, column
+// tile, reduction step) in that order of significance.
+__global__ __launch_bounds__(256) void k_pack_expert_weights(const uint16_t* __restrict__ w, int N,
+                                                             int H, int ntn, int64_t chunks,
+                                                             uint16_t* __restrict__ packed) {
+  const int nk = H / kBK;
+  for (int64_t c = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; c < chunks;
+       c += static_cast<int64_t>(gridDim.x) * 256) {
+    const int kv = static_cast<int>(c & 3);
+    const int r = static_cast<int>((c >> 2) & (kBN - 1));
+    const int64_t blk = c >> 10;
+    const int kt = static_cast<int>(blk % nk);
+    const int64_t et = blk / nk;  // expert * ntn + column tile
+    const int e = static_cast<int>(et / ntn);
+    const int n = static_cast<int>(et % ntn) * kBN + r;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (n < N) v = *reinterpret_cast<const u32x4*>(w + (static_cast<int64_t>(e) * N + n) * H + kt * kBK + kv * 8);
+    *reinterpret_cast<u32x4*>(packed + c * 8) = v;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_pack_expert_weights(const uint16_t* w, int E, int N, int H, uint16_t* packed,
+                                      hipStream_t s) {
+  const int ntn = (N + kBN - 1) / kBN;
+  const int64_t chunks = static_cast<int64_t>(E) * ntn * (H / kBK) * kBN * 4;
+  const int64_t blocks = (chunks + 255) / 256;
+  k_pack_expert_weights<<<static_cast<unsigned>(blocks < 65536 ? blocks : 65536), 256, 0, s>>>(
+      w, N, H, ntn, chunks, packed);
+  return hipGetLastError();
+}
 
 int64_t expert_gemm_max_tiles(int64_t max_rows, int E, int N) {
   return ((max_rows + kBM - 1) / kBM + E) * ((N + kBN - 1) / kBN);

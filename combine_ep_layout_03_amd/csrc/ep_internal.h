@@ -91,7 +91,7 @@ hipError_t launch_combine(const CombineArgs& a, int vec_elems, hipStream_t s);
 struct GemmArgs {
   const uint16_t* x;  // bf16 receive rows, row stride ldx elements
   int64_t ldx;
-  const uint16_t* w;  // bf16 [E, N, H]
+  const uint16_t* w;  // bf16 [E, N, H], or (packed) the tile order below
   uint16_t* y;        // bf16 output rows, row stride ldy elements
   int64_t ldy;
   const int32_t* counts;
@@ -101,11 +101,18 @@ struct GemmArgs {
   // null: x holds the expert rows; else x holds token rows and expert row r
   // reads x row row_src[r]
   const int32_t* row_src;
+  // w packed by launch_pack_expert_weights: [E][ntn][H/32][256][32], each
+  // (expert, column tile, 32-wide reduction step) block 16 KiB contiguous,
+  // rows past N zero
+  bool packed;
 };
 // H % 64 == 0, N % 128 == 0, E <= 1024, 16-byte aligned x / w / y and strides
 // (ldx % 8 == 0, ldy % 4 == 0); max_rows bounds the expert-major rows.
 // upper bound on the grouped GEMM's tiles for max_rows receive rows
 int64_t expert_gemm_max_tiles(int64_t max_rows, int E, int N);
 hipError_t launch_expert_gemm(const GemmArgs& a, int64_t max_rows, hipStream_t s);
+// w bf16 [E, N, H] -> the packed tile order of GemmArgs::w (H % 32 == 0)
+hipError_t launch_pack_expert_weights(const uint16_t* w, int E, int N, int H, uint16_t* packed,
+                                      hipStream_t s);
 
 }  // namespace ep

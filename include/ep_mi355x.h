@@ -68,6 +68,7 @@ extern "C" {
 /* ---- problem flags ---------------------------------------------------- */
 #define EP_FLAG_ZERO_PADDING 1 /* dispatch zeroes the alignment padding rows */
 #define EP_FLAG_GATHER_ROWS 2  /* ep_expert_gemm reads token rows through expert_row_src */
+#define EP_FLAG_PACKED_WEIGHTS 4 /* ep_expert_gemm's w is in ep_pack_expert_weights' order */
 
 /* ---- formats, row kinds, combine orders ------------------------------ */
 #define EP_FORMAT_BF16 0       /* receive row = the token's H bf16 values */
@@ -99,7 +100,9 @@ extern "C" {
  *               EP_FLAG_GATHER_ROWS: ep_expert_gemm takes the token rows
  *               themselves and gathers each expert row's operand through
  *               the layout's expert_row_src (dispatch fused into the GEMM).
- *               Other entry points ignore it. */
+ *               EP_FLAG_PACKED_WEIGHTS: ep_expert_gemm's weights are in the
+ *               packed tile order ep_pack_expert_weights writes.
+ *               Other entry points ignore these two. */
 typedef struct ep_problem {
   int64_t num_tokens;
   int32_t hidden;
@@ -249,13 +252,34 @@ int ep_combine(const ep_problem_t* p, const ep_layout_t* L, const int64_t* topk_
  * runs the GEMM on rows as they arrive, with no staging copy.  L must then
  * carry expert_row_src (from ep_layout) with expert_row_capacity covering
  * every expert row; the result equals the unfused dispatch + GEMM bit for
- * bit.  Requires H % 64 == 0 and n_out % 128 == 0, and
+ * bit.  With EP_FLAG_PACKED_WEIGHTS, w is the packed copy
+ * ep_pack_expert_weights made of the [E, n_out, H] weights (same E, n_out
+ * and H); the result equals the unpacked GEMM bit for bit.
+ * Requires H % 64 == 0 and n_out % 128 == 0, and
  * at most 2^31 - 1 output tiles of 320 x 256 (EP_ENOTSUP otherwise), 16-byte
  * aligned x, w and y, x_row_stride a multiple of 8 and y_row_stride a
  * multiple of 4. */
 int ep_expert_gemm(const ep_problem_t* p, const ep_layout_t* L, const void* x,
                    int64_t x_row_stride, const void* w, int32_t n_out, void* y,
                    int64_t y_row_stride, hipStream_t stream);
+
+/* Weights packed once for the grouped GEMM.  Not from the pages: a layout
+ * of this library.  Each 256-column tile of an expert's weights is stored
+ * as H/32 blocks of 256 rows x 32 elements, so every reduction step of a
+ * GEMM tile reads one contiguous 16 KiB block instead of 64 bytes from each
+ * of 256 rows 2H bytes apart; static weights are packed once and reused.
+ *   packed[e][j][k][r][c] = w[e, 256 j + r, 32 k + c]  if 256 j + r < n_out,
+ *                           0                          otherwise,
+ * for j < ceil(n_out / 256), k < H / 32, r < 256, c < 32 (bf16).
+ * ep_expert_weights_packed_bytes gives the size, E * ceil(n_out/256) * 256
+ * * H * 2 bytes, or -1 if E < 1, n_out < 1, H < 1, n_out % 128 != 0 or
+ * H % 64 != 0 (host only, no device work).  ep_pack_expert_weights writes
+ * the packed copy of w (bf16 [E, n_out, H], 16-byte aligned) to w_packed
+ * (caller-owned, that many bytes, 16-byte aligned, not overlapping w) on
+ * the stream; EP_EINVAL for null or misaligned pointers or invalid sizes. */
+int64_t ep_expert_weights_packed_bytes(int32_t num_experts, int32_t n_out, int32_t hidden);
+int ep_pack_expert_weights(const void* w, int32_t num_experts, int32_t n_out, int32_t hidden,
+                           void* w_packed, hipStream_t stream);
 
 /* Static description of a return code. */
 const char* ep_strerror(int code);

@@ -18,7 +18,17 @@ def _declared():
 
 def test_header_declares_the_boundary():
     assert _declared() == sorted(
-        ["ep_fp8_row_bytes", "ep_layout_workspace_bytes", "ep_layout", "ep_dispatch", "ep_combine", "ep_expert_gemm", "ep_strerror"]
+        [
+            "ep_fp8_row_bytes",
+            "ep_layout_workspace_bytes",
+            "ep_layout",
+            "ep_dispatch",
+            "ep_combine",
+            "ep_expert_gemm",
+            "ep_expert_weights_packed_bytes",
+            "ep_pack_expert_weights",
+            "ep_strerror",
+        ]
     )
 
 
@@ -80,6 +90,12 @@ def test_host_only_entry_points():
     assert ep.ep_layout_workspace_bytes(10, 33, 256) == 0  # K above the limit
     assert ep.ep_layout_workspace_bytes(10, 8, 1024, 8) == 0  # E + G above the limit
     assert ep.fp8_row_pitch(7168) == 7424 and ep.fp8_row_pitch(128) == 256
+    # packed expert weights: E * ceil(N / 256) * 256 * H bf16 elements
+    assert ep.ep_expert_weights_packed_bytes(256, 2048, 7168) == 256 * 2048 * 7168 * 2
+    assert ep.ep_expert_weights_packed_bytes(3, 384, 128) == 3 * 512 * 128 * 2
+    assert ep.ep_expert_weights_packed_bytes(3, 100, 128) == -1  # N % 128
+    assert ep.ep_expert_weights_packed_bytes(3, 256, 96) == -1  # H % 64
+    assert ep.ep_expert_weights_packed_bytes(0, 256, 128) == -1
     for c in range(5):
         assert ep.ep_strerror(c)
 
@@ -155,8 +171,23 @@ def test_expert_gemm_host_checks():
     lay.expert_row_capacity = 100
     assert L.ep_expert_gemm(ctypes.byref(pg), ctypes.byref(lay), fake, 0, fake, 2048, fake, 0, None) == _lib.EP_EINVAL
     # unknown flag bits
-    pu = _lib.Problem(16, 7168, 8, 256, 0, 0, 4)
+    pu = _lib.Problem(16, 7168, 8, 256, 0, 0, 8)
     assert L.ep_expert_gemm(ctypes.byref(pu), ctypes.byref(lay), fake, 0, fake, 2048, fake, 0, None) == _lib.EP_EINVAL
+
+
+def test_pack_expert_weights_host_checks():
+    """Packing rejects null or misaligned pointers and invalid sizes before
+    any launch (the pointers are placeholders that are never dereferenced)."""
+    from combine_ep_layout_03_amd import _lib
+
+    L = _lib.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    assert L.ep_pack_expert_weights(None, 4, 256, 128, fake, None) == _lib.EP_EINVAL
+    assert L.ep_pack_expert_weights(fake, 4, 256, 128, None, None) == _lib.EP_EINVAL
+    assert L.ep_pack_expert_weights(ctypes.c_void_p((1 << 20) + 8), 4, 256, 128, fake, None) == _lib.EP_EINVAL
+    assert L.ep_pack_expert_weights(fake, 4, 200, 128, fake, None) == _lib.EP_EINVAL
+    assert L.ep_pack_expert_weights(fake, 4, 256, 100, fake, None) == _lib.EP_EINVAL
+    assert L.ep_pack_expert_weights(fake, 0, 256, 128, fake, None) == _lib.EP_EINVAL
 
 
 def test_binding_rejects_host_tensors():

@@ -190,3 +190,70 @@ def test_gathered_gemm_pages_shape_equals_unfused():
     torch.cuda.synchronize()
     n = L.num_rows()
     assert torch.equal(y_fused[:n].view(torch.int16), y_unfused[:n].view(torch.int16))
+
+
+def test_pack_expert_weights_layout():
+    """The packed order is the documented permutation: block (e, j, k) holds
+    rows 256 j .. 256 j + 255 of expert e, elements 32 k .. 32 k + 31, rows
+    past N zero.  N = 384 leaves the second column tile half padding."""
+    E, N, H = 3, 384, 128
+    w = W.make_expert_weights(W.Workload("pk", T=8, H=H, K=1, E=E), N)
+    packed = ep().ep_pack_expert_weights(w.to(DEV))
+    torch.cuda.synchronize()
+    wn = u16(w).reshape(E, N, H)
+    ntn = (N + 255) // 256
+    full = np.zeros((E, ntn * 256, H), np.uint16)
+    full[:, :N] = wn
+    want = full.reshape(E, ntn, 256, H // 32, 32).transpose(0, 1, 3, 2, 4).reshape(-1)
+    assert np.array_equal(u16(packed.data), want)
+
+
+@pytest.mark.parametrize(
+    "T,K,E,H,N,A,gather",
+    [
+        (300, 2, 8, 256, 256, 0, False),
+        (700, 3, 12, 192, 384, 64, False),  # half-padded last column tile
+        (90, 2, 4, 64, 128, 0, False),
+        (1500, 2, 4, 320, 256, 0, False),
+        (600, 2, 1024, 64, 128, 0, False),
+        (700, 3, 12, 192, 384, 64, True),   # packed weights with gathered rows
+    ],
+)
+def test_packed_weights_gemm_equals_plain(T, K, E, H, N, A, gather):
+    """Packed weights change where the weight stages come from, not the
+    operands or the order: the result equals the plain GEMM bit for bit on
+    every expert row."""
+    w = W.Workload("gp", T=T, H=H, K=K, E=E, mask_p=0.1, seed=T + N)
+    idx, _ = W.make_routing(w)
+    L = ep().ep_layout(idx.to(DEV), E, expert_alignment=A, expert_row_src=gather)
+    wts = W.make_expert_weights(w, N).to(DEV)
+    packed = ep().ep_pack_expert_weights(wts)
+    if gather:
+        x = W.make_x(w).to(DEV)
+    else:
+        x = W.make_rows(w, L.max_expert_rows()).to(DEV)
+    y_plain = ep().ep_expert_gemm(x, L, wts, gather=gather)
+    y_packed = ep().ep_expert_gemm(x, L, packed, gather=gather)
+    torch.cuda.synchronize()
+    R = O.layout(idx.numpy(), E, expert_alignment=A)
+    occupied = np.zeros(y_plain.shape[0], bool)
+    for e in range(E):
+        occupied[R["offsets"][e] : R["offsets"][e] + R["counts"][e]] = True
+    assert np.array_equal(u16(y_packed)[occupied], u16(y_plain)[occupied])
+
+
+def test_packed_weights_gemm_pages_shape_equals_plain():
+    """65,536 rows x 7168 -> 2048 over 256 experts: packed and plain weights
+    give the same bytes on every expert row."""
+    w = W.by_name("pages")
+    idx, _ = W.make_routing(w)
+    L = ep().ep_layout(idx.to(DEV), w.E)
+    x = W.make_rows(w, L.max_expert_rows(), device=DEV)
+    wts = W.make_expert_weights(w, 2048, device=DEV)
+    print("packed gemm pages shape: run", flush=True)
+    packed = ep().ep_pack_expert_weights(wts)
+    y_plain = ep().ep_expert_gemm(x, L, wts)
+    y_packed = ep().ep_expert_gemm(x, L, packed)
+    torch.cuda.synchronize()
+    n = L.num_rows()
+    assert torch.equal(y_packed[:n].view(torch.int16), y_plain[:n].view(torch.int16))

@@ -10,6 +10,12 @@
  * return every token as exactly K_eff * x (fp32 sums of small integers are
  * exact, and so is their bf16 rounding).
  *
+ * The grouped GEMM then multiplies the dispatched rows by weights in
+ * {-1, 0, 1} (N = 128), once with the weights as given and once packed by
+ * ep_pack_expert_weights: every partial sum is an exact fp32 integer, so
+ * both must equal the bf16 rounding (nearest, ties to even) of the exact
+ * sum, computed here on the host.
+ *
  * Prints "OK" and exits 0 on success; prints the first mismatch and exits
  * 1 otherwise.
  */
@@ -24,6 +30,7 @@
 #define H 256
 #define K 4
 #define E 16
+#define N 128
 
 #define CHECK_HIP(x)                                                          \
   do {                                                                        \
@@ -49,6 +56,17 @@ static uint16_t bf16_of_int(int v) {
   memcpy(&b, &f, 4);
   return (uint16_t)(b >> 16); /* exact for small integers */
 }
+
+/* bf16 of an exactly representable fp32 value, round to nearest even */
+static uint16_t bf16_rne_of_int(int v) {
+  float f = (float)v;
+  uint32_t b;
+  memcpy(&b, &f, 4);
+  b += 0x7FFFu + ((b >> 16) & 1u);
+  return (uint16_t)(b >> 16);
+}
+
+static int gemm_weight(int e, int n, int h) { return (e + n * 5 + h * 7) % 3 - 1; }
 
 static int int_of_bf16(uint16_t h) {
   uint32_t b = (uint32_t)h << 16;
@@ -197,6 +215,61 @@ int main(void) {
       }
     }
 
+  /* grouped GEMM over the expert-major rows, plain and packed weights */
+  {
+    static uint16_t wg[E * N * H];
+    static uint16_t y[T * K * N], yp[T * K * N];
+    static int row_t[T * K], row_e[T * K];
+    int n, r;
+    for (e = 0; e < E; ++e)
+      for (n = 0; n < N; ++n)
+        for (h = 0; h < H; ++h) wg[(e * N + n) * H + h] = bf16_of_int(gemm_weight(e, n, h));
+    for (t = 0; t < T * K; ++t) {
+      const int64_t id = idx[t];
+      if (id >= 0 && id < E) {
+        row_t[slot[t]] = t / K;
+        row_e[slot[t]] = (int)id;
+      }
+    }
+    const int64_t packed_bytes = ep_expert_weights_packed_bytes(E, N, H);
+    if (packed_bytes != (int64_t)E * 256 * H * 2 || ep_expert_weights_packed_bytes(E, 100, H) != -1) {
+      printf("ep_expert_weights_packed_bytes gave %lld\n", (long long)packed_bytes);
+      return 1;
+    }
+    uint16_t *d_wg, *d_wp, *d_y, *d_yp;
+    CHECK_HIP(hipMalloc((void**)&d_wg, sizeof wg));
+    CHECK_HIP(hipMalloc((void**)&d_wp, (size_t)packed_bytes));
+    CHECK_HIP(hipMalloc((void**)&d_y, sizeof y));
+    CHECK_HIP(hipMalloc((void**)&d_yp, sizeof yp));
+    CHECK_HIP(hipMemcpy(d_wg, wg, sizeof wg, hipMemcpyHostToDevice));
+    CHECK_EP(ep_expert_gemm(&p, &L, d_recv, 0, d_wg, N, d_y, 0, s));
+    CHECK_EP(ep_pack_expert_weights(d_wg, E, N, H, d_wp, s));
+    {
+      ep_problem_t q = p;
+      q.flags = EP_FLAG_PACKED_WEIGHTS;
+      CHECK_EP(ep_expert_gemm(&q, &L, d_recv, 0, d_wp, N, d_yp, 0, s));
+    }
+    CHECK_HIP(hipStreamSynchronize(s));
+    CHECK_HIP(hipMemcpy(y, d_y, sizeof y, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(yp, d_yp, sizeof yp, hipMemcpyDeviceToHost));
+    for (r = 0; r < n_sel; ++r)
+      for (n = 0; n < N; ++n) {
+        int sum = 0;
+        for (h = 0; h < H; ++h)
+          sum += ((row_t[r] * 13 + h * 7) % 17 - 8) * gemm_weight(row_e[r], n, h);
+        const uint16_t want = bf16_rne_of_int(sum);
+        if (y[r * N + n] != want || yp[r * N + n] != want) {
+          printf("gemm row %d column %d: got %04x / packed %04x, expected %04x (sum %d)\n", r, n,
+                 y[r * N + n], yp[r * N + n], want, sum);
+          return 1;
+        }
+      }
+    hipFree(d_wg);
+    hipFree(d_wp);
+    hipFree(d_y);
+    hipFree(d_yp);
+  }
+
   hipFree(d_idx);
   hipFree(d_w);
   hipFree(d_x);
@@ -208,7 +281,8 @@ int main(void) {
   hipFree(d_status);
   hipFree(d_ws);
   hipStreamDestroy(s);
-  printf("OK: %d selections, %d invalid ids, combine of the dispatched rows = K_eff * x\n", n_sel,
-         n_invalid);
+  printf("OK: %d selections, %d invalid ids, combine of the dispatched rows = K_eff * x, "
+         "grouped GEMM exact (plain and packed weights)\n",
+         n_sel, n_invalid);
   return 0;
 }

@@ -1,7 +1,9 @@
 """The C ABI from plain C: tests/c/ep_c_roundtrip.c (C99, built by gcc
 against include/ep_mi355x.h alone) runs layout, bf16 dispatch and combine on
 the GPU and checks closed forms: status words, slots forming a permutation,
-and the unit-weight combine of the dispatched rows equal to K_eff * x."""
+the unit-weight combine of the dispatched rows equal to K_eff * x, and the
+grouped GEMM on small integers (plain and packed weights) equal to the bf16
+rounding of the exact sums."""
 import os
 import subprocess
 

@@ -238,8 +238,14 @@ int64_t ep_expert_weights_packed_bytes(int32_t num_experts, int32_t n_out, int32
 
 int ep_pack_expert_weights(const void* w, int32_t num_experts, int32_t n_out, int32_t hidden,
                            void* w_packed, hipStream_t stream) {
-  if (ep_expert_weights_packed_bytes(num_experts, n_out, hidden) < 0) return EP_EINVAL;
+  const int64_t packed_bytes = ep_expert_weights_packed_bytes(num_experts, n_out, hidden);
+  if (packed_bytes < 0) return EP_EINVAL;
   if (!w || !w_packed || !aligned(w, 16) || !aligned(w_packed, 16)) return EP_EINVAL;
+  // the copy reads w while writing w_packed: the two must not overlap
+  const uintptr_t w0 = reinterpret_cast<uintptr_t>(w);
+  const uintptr_t p0 = reinterpret_cast<uintptr_t>(w_packed);
+  const uintptr_t w_bytes = static_cast<uintptr_t>(num_experts) * n_out * hidden * 2;
+  if (w0 < p0 + static_cast<uintptr_t>(packed_bytes) && p0 < w0 + w_bytes) return EP_EINVAL;
   return ep::launch_pack_expert_weights(static_cast<const uint16_t*>(w), num_experts, n_out, hidden,
                                         static_cast<uint16_t*>(w_packed), stream) == hipSuccess
              ? EP_OK

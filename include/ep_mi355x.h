@@ -276,7 +276,8 @@ int ep_expert_gemm(const ep_problem_t* p, const ep_layout_t* L, const void* x,
  * H % 64 != 0 (host only, no device work).  ep_pack_expert_weights writes
  * the packed copy of w (bf16 [E, n_out, H], 16-byte aligned) to w_packed
  * (caller-owned, that many bytes, 16-byte aligned, not overlapping w) on
- * the stream; EP_EINVAL for null or misaligned pointers or invalid sizes. */
+ * the stream; EP_EINVAL for null, misaligned or overlapping pointers or
+ * invalid sizes. */
 int64_t ep_expert_weights_packed_bytes(int32_t num_experts, int32_t n_out, int32_t hidden);
 int ep_pack_expert_weights(const void* w, int32_t num_experts, int32_t n_out, int32_t hidden,
                            void* w_packed, hipStream_t stream);

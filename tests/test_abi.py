@@ -188,6 +188,10 @@ def test_pack_expert_weights_host_checks():
     assert L.ep_pack_expert_weights(fake, 4, 200, 128, fake, None) == _lib.EP_EINVAL
     assert L.ep_pack_expert_weights(fake, 4, 256, 100, fake, None) == _lib.EP_EINVAL
     assert L.ep_pack_expert_weights(fake, 0, 256, 128, fake, None) == _lib.EP_EINVAL
+    # source and destination overlapping (4 x 256 x 128 bf16 = 256 KiB each)
+    assert L.ep_pack_expert_weights(fake, 4, 256, 128, fake, None) == _lib.EP_EINVAL
+    assert L.ep_pack_expert_weights(fake, 4, 256, 128, ctypes.c_void_p((1 << 20) + (128 << 10)), None) == _lib.EP_EINVAL
+    assert L.ep_pack_expert_weights(ctypes.c_void_p((1 << 20) + (128 << 10)), 4, 256, 128, fake, None) == _lib.EP_EINVAL
 
 
 def test_binding_rejects_host_tensors():

@@ -24,7 +24,10 @@
 // 7168, top-8 of 256: 200 us with contiguous per-wave ranges on a resident
 // grid (concurrent reads span the whole expert-output buffer), 195 us with
 // the cyclic walk on that grid, 183.5 us with one wave per item.
-// Expert-output rows are read exactly once, with non-temporal buffer loads.
+// Expert-output rows are read exactly once, with non-temporal buffer loads,
+// and output rows are written with non-temporal stores: with the
+// token-ordered window this measured the same for the flat order and 5-9%
+// faster for the grouped order (1569 -> 1435 us at 65,536 tokens).
 #include <limits.h>
 
 #include "ep_device.h"
@@ -198,7 +201,7 @@ __device__ __forceinline__ void reduce_chunk(const CombineArgs& a, int64_t t,
       res[e] = GROUPED ? __fadd_rn(tot, P) : P;
     }
     const int vi = vb + u * kWave + lane;
-    if (vi < nvec) outv[vi] = B::pack(res);
+    if (vi < nvec) nt_store(B::pack(res), outv + vi);
   }
 }
 
@@ -222,7 +225,7 @@ __device__ __forceinline__ void empty_chunk(const CombineArgs& a, int64_t t,
       const float seed = bias_seed<VE, NB>(bias, e);
       res[e] = GROUPED ? __fadd_rn(seed, 0.0f) : seed;
     }
-    outv[vi] = B::pack(res);
+    nt_store(B::pack(res), outv + vi);
   }
 }
 

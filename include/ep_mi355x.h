@@ -31,6 +31,9 @@
  *     status words (EP_STATUS_*), never by corrupting memory.
  *   - bf16 values are 16-bit IEEE-style bfloat16 bit patterns; fp32 is IEEE
  *     binary32; all integers are little-endian.
+ *   - The environment variable EP_MI355X_GRID_BLOCKS=<n> (1 <= n <= 2^20),
+ *     read at every launch, replaces the grid size of the dispatch and
+ *     combine kernels, for launch sweeps; results are the same at any grid.
  */
 #ifndef EP_MI355X_H
 #define EP_MI355X_H

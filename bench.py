@@ -196,10 +196,14 @@ def time_extras(ep, W, w, d_idx, d_wt, x, y, L, n_sel, rb, pitch, reps, only=Non
 
             us_f = timed(lambda: ep.ep_expert_gemm(x, Lf, wts, out=yg, gather=True), gemm_reps)
             us_u = timed(unfused, gemm_reps)
+            packed = ep.ep_pack_expert_weights(wts)
+            us_fp = timed(lambda: ep.ep_expert_gemm(x, Lf, packed, out=yg, gather=True), gemm_reps)
+            del packed
             fbytes = E * N * H * 2 + T * H * 2 + n_sel * N * 2
             res["expert_gemm_fused_dispatch_n2048"] = {
                 "us": round(us_f, 1),
                 "us_dispatch_then_gemm": round(us_u, 1),
+                "us_packed_weights": round(us_fp, 1),
                 "TFLOPs": round(flops / (us_f * 1e-6) / 1e12, 1),
                 "bytes": int(fbytes),
                 "GBps": round(fbytes / (us_f * 1e-6) / 1e9, 1),

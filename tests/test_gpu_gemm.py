@@ -257,3 +257,54 @@ def test_packed_weights_gemm_pages_shape_equals_plain():
     torch.cuda.synchronize()
     n = L.num_rows()
     assert torch.equal(y_packed[:n].view(torch.int16), y_plain[:n].view(torch.int16))
+
+
+def _gemm_cases(n=8, seed=77):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E = int(rng.choice([1, 5, 16, 64, 300]))
+        out.append(
+            dict(
+                T=int(rng.integers(20, 1200)),
+                K=int(min(rng.integers(1, 9), E)),
+                E=E,
+                H=int(64 * rng.integers(1, 7)),
+                N=int(128 * rng.integers(1, 5)),
+                A=int(rng.choice([0, 0, 8, 64])),
+                gather=bool(rng.random() < 0.4),
+                seed=500 + i,
+            )
+        )
+    return out
+
+
+@pytest.mark.parametrize("c", _gemm_cases(), ids=lambda c: f"E{c['E']}-H{c['H']}-N{c['N']}-A{c['A']}-g{int(c['gather'])}")
+def test_expert_gemm_random_shapes(c):
+    """Seeded random shapes: within the oracle's bound, and packed weights
+    bit-identical to plain ones."""
+    print("random gemm", c, flush=True)
+    w = W.Workload("gr", T=c["T"], H=c["H"], K=c["K"], E=c["E"], mask_p=0.1, seed=c["seed"])
+    idx, _ = W.make_routing(w)
+    A = c["A"]
+    R = O.layout(idx.numpy(), w.E, expert_alignment=A)
+    L = ep().ep_layout(idx.to(DEV), w.E, expert_alignment=A, expert_row_src=c["gather"])
+    wts = W.make_expert_weights(w, c["N"])
+    if c["gather"]:
+        x = W.make_x(w)
+        rows = O.dispatch_bf16(u16(x), R["slot"], R["n_rows_expert"])
+    else:
+        x = W.make_rows(w, L.max_expert_rows())
+        rows = None
+    y = ep().ep_expert_gemm(x.to(DEV), L, wts.to(DEV), gather=c["gather"])
+    yp = ep().ep_expert_gemm(x.to(DEV), L, ep().ep_pack_expert_weights(wts.to(DEV)), gather=c["gather"])
+    torch.cuda.synchronize()
+    n = R["n_rows_expert"]
+    occupied = np.zeros(n, bool)
+    for e in range(w.E):
+        occupied[R["offsets"][e] : R["offsets"][e] + R["counts"][e]] = True
+    got = u16(y)[:n]
+    assert np.array_equal(u16(yp)[:n][occupied], got[occupied])
+    xin = rows if rows is not None else u16(x)[:n]
+    if occupied.any():
+        _check(got, xin, R["counts"], R["offsets"], u16(wts))

@@ -296,8 +296,11 @@ def test_expert_gemm_random_shapes(c):
     else:
         x = W.make_rows(w, L.max_expert_rows())
         rows = None
-    y = ep().ep_expert_gemm(x.to(DEV), L, wts.to(DEV), gather=c["gather"])
-    yp = ep().ep_expert_gemm(x.to(DEV), L, ep().ep_pack_expert_weights(wts.to(DEV)), gather=c["gather"])
+    # padding rows are never written: start from zeros so they hold no NaN patterns
+    y = torch.zeros(L.max_expert_rows(), c["N"], dtype=torch.bfloat16, device=DEV)
+    yp = torch.zeros_like(y)
+    ep().ep_expert_gemm(x.to(DEV), L, wts.to(DEV), out=y, gather=c["gather"])
+    ep().ep_expert_gemm(x.to(DEV), L, ep().ep_pack_expert_weights(wts.to(DEV)), out=yp, gather=c["gather"])
     torch.cuda.synchronize()
     n = R["n_rows_expert"]
     occupied = np.zeros(n, bool)

@@ -32,6 +32,21 @@ __device__ __forceinline__ bool first_in_group(const int64_t* __restrict__ idx, 
   return true;
 }
 
+// The same test from the neighbouring lanes, when K divides the wave size:
+// every block, round and wave starts at an entry index that is a multiple of
+// 64, so lanes (lane & ~(K-1)) .. + K-1 hold one token's K entries in k
+// order.  g is this entry's group, or -1 when it is not valid.  Every lane of
+// the wave must call this (the shuffles read the other lanes).
+__device__ __forceinline__ bool first_in_group_lanes(int g, int K, int lane) {
+  const int base = lane & ~(K - 1);
+  bool first = g >= 0;
+  for (int j = 0; j < K; ++j) {
+    const int gj = __shfl(g, base + j, kWave);
+    if (base + j < lane && gj == g) first = false;
+  }
+  return first;
+}
+
 template <bool GROUPED>
 __global__ __launch_bounds__(kBlock) void k_layout_count(const int64_t* __restrict__ idx,
                                                          uint32_t n, int K, int E, int epg,
@@ -41,21 +56,26 @@ __global__ __launch_bounds__(kBlock) void k_layout_count(const int64_t* __restri
   for (int c = threadIdx.x; c < ncols; c += kBlock) cnt[c] = 0;
   __syncthreads();
   const uint32_t base = blockIdx.x * static_cast<uint32_t>(rounds) * kBlock;
+  const bool lanes = GROUPED && kWave % K == 0;  // a token's entries in neighbouring lanes
+  const int lane = threadIdx.x & (kWave - 1);
   for (int r = 0; r < rounds; ++r) {
     const uint32_t i = base + static_cast<uint32_t>(r) * kBlock + threadIdx.x;
-    if (i >= n) break;
-    const int64_t v = idx[i];
-    if (v >= 0 && v < E) {
-      const int e = static_cast<int>(v);
-      atomicAdd(&cnt[e], 1);
-      if (GROUPED) {
+    const bool in = i < n;
+    const int64_t v = in ? idx[i] : -1;
+    const bool valid = v >= 0 && v < E;
+    const int e = valid ? static_cast<int>(v) : -1;
+    if (valid) atomicAdd(&cnt[e], 1);
+    else if (v != -1) atomicAdd(&cnt[ncols - 1], 1);
+    if (GROUPED) {
+      if (lanes) {
+        const int g = valid ? e / epg : -1;
+        if (first_in_group_lanes(g, K, lane)) atomicAdd(&cnt[E + g], 1);
+      } else if (valid) {
         const uint32_t t = i / static_cast<uint32_t>(K);
         const int k = static_cast<int>(i - t * static_cast<uint32_t>(K));
         const int g = e / epg;
         if (first_in_group(idx, t, k, K, E, epg, g)) atomicAdd(&cnt[E + g], 1);
       }
-    } else if (v != -1) {
-      atomicAdd(&cnt[ncols - 1], 1);
     }
   }
   __syncthreads();
@@ -191,6 +211,7 @@ __global__ __launch_bounds__(kBlock) void k_layout_place(LayoutArgs a, int ncols
   uint64_t* wbm = bm + wave * nkeys;
   const uint64_t bit = 1ull << lane;
   const uint64_t lt = lanemask_lt();
+  const bool lanes = GROUPED && kWave % a.K == 0;  // a token's entries in neighbouring lanes
   for (int r = 0; r < rounds; ++r) {
     const uint32_t i = base + static_cast<uint32_t>(r) * kBlock + tid;
     const bool in = i < a.n;
@@ -203,7 +224,11 @@ __global__ __launch_bounds__(kBlock) void k_layout_place(LayoutArgs a, int ncols
     const int e = valid ? static_cast<int>(v) : -1;
     int kg = -1, g = 0;
     uint32_t t = 0;
-    if (GROUPED && valid) {
+    if (GROUPED && lanes) {
+      g = valid ? e / a.epg : -1;
+      t = i / static_cast<uint32_t>(a.K);
+      if (first_in_group_lanes(g, a.K, lane)) kg = E + g;
+    } else if (GROUPED && valid) {
       t = i / static_cast<uint32_t>(a.K);
       const int k = static_cast<int>(i - t * static_cast<uint32_t>(a.K));
       g = e / a.epg;
@@ -234,7 +259,32 @@ __global__ __launch_bounds__(kBlock) void k_layout_place(LayoutArgs a, int ncols
     }
     if (in) a.slot[i] = e >= 0 ? sbase[e] + rankE : -1;
     if (erows_ok && e >= 0) a.expert_row_src[sbase[e] + rankE] = static_cast<int>(i / static_cast<uint32_t>(a.K));
-    if (GROUPED && in) {
+    if (GROUPED && lanes) {
+      // The token's K lanes share the rows its first-in-group lanes claimed:
+      // each lane writes its own grow entry and its own position k of every
+      // row of its token (coalesced across the K lanes).
+      const int row = kg >= 0 ? sbase[kg] + rankG : -1;
+      const int tb = lane & ~(a.K - 1);
+      const int k = lane - tb;
+      const int loc = valid ? e - g * a.epg : -1;
+      const float wv = lists_ok && valid ? a.w[i] : 0.0f;
+      int myrow = -1;
+      for (int j = 0; j < a.K; ++j) {
+        const int rj = __shfl(row, tb + j, kWave);  // row claimed by entry j, or -1
+        const int gj = __shfl(g, tb + j, kWave);
+        if (rj >= 0) {
+          const bool same = valid && gj == g;
+          if (same) myrow = rj;
+          if (lists_ok) {
+            const size_t rk = static_cast<size_t>(rj) * a.K + k;
+            a.row_idx[rk] = same ? loc : -1;
+            a.row_w[rk] = same ? wv : 0.0f;
+          }
+        }
+      }
+      if (in) a.grow[i] = myrow;
+      if (kg >= 0 && lists_ok) a.row_src[row] = static_cast<int>(t);
+    } else if (GROUPED && in) {
       if (!valid) a.grow[i] = -1;
       if (kg >= 0) {
         const int row = sbase[kg] + rankG;

@@ -58,10 +58,15 @@ __global__ __launch_bounds__(kBlock) void k_layout_count(const int64_t* __restri
   const uint32_t base = blockIdx.x * static_cast<uint32_t>(rounds) * kBlock;
   const bool lanes = GROUPED && kWave % K == 0;  // a token's entries in neighbouring lanes
   const int lane = threadIdx.x & (kWave - 1);
+  // each round's id is loaded one round ahead
+  int64_t v_next = base + threadIdx.x < n ? idx[base + threadIdx.x] : -1;
   for (int r = 0; r < rounds; ++r) {
     const uint32_t i = base + static_cast<uint32_t>(r) * kBlock + threadIdx.x;
-    const bool in = i < n;
-    const int64_t v = in ? idx[i] : -1;
+    const int64_t v = v_next;
+    if (r + 1 < rounds) {
+      const uint32_t i2 = i + kBlock;
+      v_next = i2 < n ? idx[i2] : -1;
+    }
     const bool valid = v >= 0 && v < E;
     const int e = valid ? static_cast<int>(v) : -1;
     if (valid) atomicAdd(&cnt[e], 1);
@@ -212,13 +217,18 @@ __global__ __launch_bounds__(kBlock) void k_layout_place(LayoutArgs a, int ncols
   const uint64_t bit = 1ull << lane;
   const uint64_t lt = lanemask_lt();
   const bool lanes = GROUPED && kWave % a.K == 0;  // a token's entries in neighbouring lanes
+  // the lanes path loads each round's weights one round ahead, with the ids
+  const bool want_w = lanes && lists_ok && a.row_cap > 0 && a.w != nullptr;
+  float w_next = want_w && base + tid < a.n ? a.w[base + tid] : 0.0f;
   for (int r = 0; r < rounds; ++r) {
     const uint32_t i = base + static_cast<uint32_t>(r) * kBlock + tid;
     const bool in = i < a.n;
     const int64_t v = v_next;
+    const float w_cur = w_next;
     if (r + 1 < rounds) {
       const uint32_t i2 = i + kBlock;
       v_next = i2 < a.n ? a.idx[i2] : -1;
+      if (want_w) w_next = i2 < a.n ? a.w[i2] : 0.0f;
     }
     const bool valid = in && v >= 0 && v < E;
     const int e = valid ? static_cast<int>(v) : -1;
@@ -267,7 +277,7 @@ __global__ __launch_bounds__(kBlock) void k_layout_place(LayoutArgs a, int ncols
       const int tb = lane & ~(a.K - 1);
       const int k = lane - tb;
       const int loc = valid ? e - g * a.epg : -1;
-      const float wv = lists_ok && valid ? a.w[i] : 0.0f;
+      const float wv = valid ? w_cur : 0.0f;
       int myrow = -1;
       for (int j = 0; j < a.K; ++j) {
         const int rj = __shfl(row, tb + j, kWave);  // row claimed by entry j, or -1

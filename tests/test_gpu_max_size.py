@@ -153,3 +153,35 @@ def test_max_selection_count():
     say("combine (random weights) ok on sampled tokens")
     del idx, L, x, recv, wt, out, keff
     torch.cuda.empty_cache()
+
+
+def test_large_hidden_bf16():
+    """Hidden 2^20 + 8 (2 MiB rows, a ragged last chunk): bf16 dispatch and
+    flat and grouped combine against the oracle element by element; offsets
+    inside a row stay 32-bit there (row bytes < 2^32)."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import combine_ep_layout_03_amd as ep
+    import workloads as W
+
+    w = W.Workload("wide", T=48, H=(1 << 20) + 8, K=4, E=8, G=2, mask_p=0.2, full_mask_frac=0.05, seed=5)
+    say(f"large hidden: T={w.T} H={w.H} K={w.K} E={w.E}")
+    idx, wt = W.make_routing(w)
+    x = W.make_x(w)
+    R = O.layout(idx.numpy(), w.E)
+    L = ep.ep_layout(idx.to(DEV), w.E)
+    recv = ep.ep_dispatch(x.to(DEV), L)
+    torch.cuda.synchronize()
+    n = R["n_sel"]
+    assert np.array_equal(u16(recv[:n]), O.dispatch_bf16(u16(x), R["slot"], n))
+    say("dispatch ok")
+    y = W.make_y(w, rows=n)
+    out = ep.ep_combine(y.to(DEV), L, wt.to(DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(u16(out), O.combine(u16(y), R["slot"], wt.numpy()))
+    d_idx = idx.to(DEV)
+    Lg = ep.ep_layout(d_idx, w.E, w.G, wt.to(DEV))  # the grouped order needs the groups
+    outg = ep.ep_combine(y.to(DEV), Lg, wt.to(DEV), topk_idx=d_idx, order=ep.EP_COMBINE_GROUPED)
+    torch.cuda.synchronize()
+    assert np.array_equal(u16(outg), O.combine_grouped(u16(y), idx.numpy(), R["slot"], wt.numpy(), w.E, w.G))
+    say("combine (flat and grouped) ok")

@@ -1,14 +1,23 @@
 /*
- * The C ABI used from plain C (C99, built with gcc): layout, bf16 dispatch
- * and combine on one GPU, checked against closed forms rather than an
- * oracle.
+ * The C ABI used from plain C (C99, built with gcc): layout, bf16 and fp8
+ * dispatch, flat and grouped combine, grouped rows and the grouped GEMM on
+ * one GPU, checked against closed forms rather than an oracle.
  *
  * Routing: T tokens pick K distinct experts (e = (7t + 5k) mod E); some
  * entries are masked (-1) and one id is out of range (counted in the
- * invalid-id status word and treated as -1).  Token rows hold small
- * integers, so the combine of the dispatched rows with unit weights must
+ * invalid-id status word and treated as -1).  Token rows hold integers in
+ * [-7, 7], so the combine of the dispatched rows with unit weights must
  * return every token as exactly K_eff * x (fp32 sums of small integers are
  * exact, and so is their bf16 rounding).
+ *
+ * The fp8 dispatch of the same rows: every 128-element group holds the values
+ * -7..7 (period 15 along h), so its amax is 7, its scale 7/448 = 2^-6 exactly,
+ * and every payload byte is the E4M3FN code of 64 * x, an exactly
+ * representable value (64 .. 448), so the packed row is known byte for byte.
+ *
+ * Grouped rows (G = 4 groups of 4 experts): every selection's group row holds
+ * its token's row, the row lists name the token and its local experts, and
+ * the grouped-order combine of the expert rows is again K_eff * x.
  *
  * The grouped GEMM then multiplies the dispatched rows by weights in
  * {-1, 0, 1} (N = 128), once with the weights as given and once packed by
@@ -66,6 +75,12 @@ static uint16_t bf16_rne_of_int(int v) {
   return (uint16_t)(b >> 16);
 }
 
+/* E4M3FN code of 64 * v for an integer v in [-7, 7]: 2^6 .. 1.75 * 2^8 */
+static uint8_t e4m3_of_64x(int v) {
+  static const uint8_t mag[8] = {0x00, 0x68, 0x70, 0x74, 0x78, 0x7A, 0x7C, 0x7E};
+  return (uint8_t)(mag[v < 0 ? -v : v] | (v < 0 ? 0x80 : 0x00));
+}
+
 static int gemm_weight(int e, int n, int h) { return (e + n * 5 + h * 7) % 3 - 1; }
 
 static int int_of_bf16(uint16_t h) {
@@ -100,7 +115,7 @@ int main(void) {
         ++n_invalid;
       }
     }
-    for (h = 0; h < H; ++h) x[t * H + h] = bf16_of_int((t * 13 + h * 7) % 17 - 8);
+    for (h = 0; h < H; ++h) x[t * H + h] = bf16_of_int((t * 13 + h * 7) % 15 - 7);
   }
 
   ep_problem_t p;
@@ -207,13 +222,156 @@ int main(void) {
   }
   for (t = 0; t < T; ++t)
     for (h = 0; h < H; ++h) {
-      const int want = keff[t] * ((t * 13 + h * 7) % 17 - 8);
+      const int want = keff[t] * ((t * 13 + h * 7) % 15 - 7);
       const int got = int_of_bf16(out[t * H + h]);
       if (got != want) {
         printf("token %d element %d: combine gave %d, expected %d\n", t, h, got, want);
         return 1;
       }
     }
+
+  /* fp8 dispatch: payload, scales and padding of every packed row */
+  {
+    const int64_t rb = ep_fp8_row_bytes(H);
+    static uint8_t recv8[(size_t)T * K * 272];
+    uint8_t* d_recv8;
+    if (rb != 272) {
+      printf("fp8 row bytes %lld, expected 272\n", (long long)rb);
+      return 1;
+    }
+    CHECK_HIP(hipMalloc((void**)&d_recv8, (size_t)T * K * rb));
+    CHECK_EP(ep_dispatch(&p, &L, d_x, d_recv8, T * K, 0, EP_ROWS_EXPERT, EP_FORMAT_FP8_PACKED, s));
+    CHECK_HIP(hipStreamSynchronize(s));
+    CHECK_HIP(hipMemcpy(recv8, d_recv8, (size_t)n_sel * rb, hipMemcpyDeviceToHost));
+    for (t = 0; t < T * K; ++t) {
+      if (slot[t] < 0) continue;
+      const uint8_t* row = recv8 + (size_t)slot[t] * rb;
+      const int tok = t / K;
+      for (h = 0; h < H; ++h)
+        if (row[h] != e4m3_of_64x((tok * 13 + h * 7) % 15 - 7)) {
+          printf("fp8 row of entry %d, byte %d: %02x, expected %02x\n", t, h, row[h],
+                 e4m3_of_64x((tok * 13 + h * 7) % 15 - 7));
+          return 1;
+        }
+      for (h = H; h < rb; ++h) {
+        /* scales 2^-6 = 0x3C800000 little-endian, then zero padding */
+        const int i = h - H;
+        const uint8_t want = i < 4 * (H / 128) ? (uint8_t[]){0x00, 0x00, 0x80, 0x3C}[i % 4] : 0;
+        if (row[h] != want) {
+          printf("fp8 row of entry %d, tail byte %d: %02x, expected %02x\n", t, i, row[h], want);
+          return 1;
+        }
+      }
+    }
+    hipFree(d_recv8);
+  }
+
+  /* grouped rows and the grouped combine order */
+  {
+    enum { G = 4, EPG = E / G };
+    ep_problem_t pg = p;
+    pg.num_groups = G;
+    static int32_t grow[T * K], rsrc[T * G], ridx[T * G * K], gcounts[G];
+    static float rw[T * G * K];
+    static uint16_t recvg[T * G * H], outg[T * H];
+    int32_t *d_gcounts, *d_goffsets, *d_grow, *d_rsrc, *d_ridx;
+    float* d_rw;
+    uint16_t *d_recvg, *d_outg;
+    void* d_wsg;
+    const size_t wsg_bytes = ep_layout_workspace_bytes(&pg);
+    CHECK_HIP(hipMalloc((void**)&d_gcounts, G * 4));
+    CHECK_HIP(hipMalloc((void**)&d_goffsets, (G + 1) * 4));
+    CHECK_HIP(hipMalloc((void**)&d_grow, T * K * 4));
+    CHECK_HIP(hipMalloc((void**)&d_rsrc, T * G * 4));
+    CHECK_HIP(hipMalloc((void**)&d_ridx, T * G * K * 4));
+    CHECK_HIP(hipMalloc((void**)&d_rw, T * G * K * 4));
+    CHECK_HIP(hipMalloc((void**)&d_recvg, sizeof recvg));
+    CHECK_HIP(hipMalloc((void**)&d_outg, sizeof outg));
+    CHECK_HIP(hipMalloc(&d_wsg, wsg_bytes));
+    ep_layout_t Lg = L;
+    Lg.group_counts = d_gcounts;
+    Lg.group_offsets = d_goffsets;
+    Lg.grow = d_grow;
+    Lg.row_src = d_rsrc;
+    Lg.row_topk_idx = d_ridx;
+    Lg.row_topk_weights = d_rw;
+    Lg.row_capacity = T * G;
+    CHECK_EP(ep_layout(&pg, d_idx, d_w, &Lg, d_wsg, wsg_bytes, s));
+    CHECK_EP(ep_dispatch(&pg, &Lg, d_x, d_recvg, T * G, 0, EP_ROWS_GROUP, EP_FORMAT_BF16, s));
+    CHECK_EP(ep_combine(&pg, &Lg, d_idx, d_w, d_recv, T * K, NULL, NULL, d_outg, EP_COMBINE_GROUPED, s));
+    CHECK_HIP(hipStreamSynchronize(s));
+    CHECK_HIP(hipMemcpy(status, d_status, sizeof status, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(gcounts, d_gcounts, sizeof gcounts, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(grow, d_grow, sizeof grow, hipMemcpyDeviceToHost));
+    const int R = status[EP_STATUS_ROWS_GROUP];
+    CHECK_HIP(hipMemcpy(rsrc, d_rsrc, (size_t)R * 4, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(ridx, d_ridx, (size_t)R * K * 4, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(rw, d_rw, (size_t)R * K * 4, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(recvg, d_recvg, (size_t)R * H * 2, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(outg, d_outg, sizeof outg, hipMemcpyDeviceToHost));
+    {
+      int hits = 0, sum = 0, g;
+      for (t = 0; t < T; ++t)
+        for (g = 0; g < G; ++g) {
+          int hit = 0;
+          for (k = 0; k < K; ++k) {
+            const int64_t id = idx[t * K + k];
+            if (id >= 0 && id < E && id / EPG == g) hit = 1;
+          }
+          hits += hit;
+        }
+      for (g = 0; g < G; ++g) sum += gcounts[g];
+      if (R != hits || sum != hits || status[EP_STATUS_LIST_OVERFLOW] != 0) {
+        printf("grouped rows %d (group counts sum %d), expected %d\n", R, sum, hits);
+        return 1;
+      }
+    }
+    for (t = 0; t < T * K; ++t) {
+      const int64_t id = idx[t];
+      const int tok = t / K;
+      if (!(id >= 0 && id < E)) {
+        if (grow[t] != -1) {
+          printf("entry %d: no selection but group row %d\n", t, grow[t]);
+          return 1;
+        }
+        continue;
+      }
+      const int r = grow[t];
+      if (r < 0 || r >= R || rsrc[r] != tok) {
+        printf("entry %d: group row %d of token %d\n", t, r, r >= 0 && r < R ? rsrc[r] : -1);
+        return 1;
+      }
+      for (k = 0; k < K; ++k) {
+        const int64_t id2 = idx[tok * K + k];
+        const int same = id2 >= 0 && id2 < E && id2 / EPG == id / EPG;
+        if (ridx[r * K + k] != (same ? (int)(id2 - (id / EPG) * EPG) : -1) ||
+            rw[r * K + k] != (same ? w[tok * K + k] : 0.0f)) {
+          printf("row %d list entry %d: %d %g\n", r, k, ridx[r * K + k], rw[r * K + k]);
+          return 1;
+        }
+      }
+      for (h = 0; h < H; ++h)
+        if (recvg[(size_t)r * H + h] != x[tok * H + h]) {
+          printf("group row %d element %d differs from token %d\n", r, h, tok);
+          return 1;
+        }
+    }
+    for (t = 0; t < T; ++t)
+      for (h = 0; h < H; ++h)
+        if (int_of_bf16(outg[t * H + h]) != keff[t] * ((t * 13 + h * 7) % 15 - 7)) {
+          printf("grouped combine, token %d element %d: %d\n", t, h, int_of_bf16(outg[t * H + h]));
+          return 1;
+        }
+    hipFree(d_gcounts);
+    hipFree(d_goffsets);
+    hipFree(d_grow);
+    hipFree(d_rsrc);
+    hipFree(d_ridx);
+    hipFree(d_rw);
+    hipFree(d_recvg);
+    hipFree(d_outg);
+    hipFree(d_wsg);
+  }
 
   /* grouped GEMM over the expert-major rows, plain and packed weights */
   {
@@ -256,7 +414,7 @@ int main(void) {
       for (n = 0; n < N; ++n) {
         int sum = 0;
         for (h = 0; h < H; ++h)
-          sum += ((row_t[r] * 13 + h * 7) % 17 - 8) * gemm_weight(row_e[r], n, h);
+          sum += ((row_t[r] * 13 + h * 7) % 15 - 7) * gemm_weight(row_e[r], n, h);
         const uint16_t want = bf16_rne_of_int(sum);
         if (y[r * N + n] != want || yp[r * N + n] != want) {
           printf("gemm row %d column %d: got %04x / packed %04x, expected %04x (sum %d)\n", r, n,
@@ -282,6 +440,7 @@ int main(void) {
   hipFree(d_ws);
   hipStreamDestroy(s);
   printf("OK: %d selections, %d invalid ids, combine of the dispatched rows = K_eff * x, "
+         "fp8 rows exact, grouped rows, lists and grouped combine exact, "
          "grouped GEMM exact (plain and packed weights)\n",
          n_sel, n_invalid);
   return 0;

@@ -1,9 +1,11 @@
 """The C ABI from plain C: tests/c/ep_c_roundtrip.c (C99, built by gcc
 against include/ep_mi355x.h alone) runs layout, bf16 dispatch and combine on
 the GPU and checks closed forms: status words, slots forming a permutation,
-the unit-weight combine of the dispatched rows equal to K_eff * x, and the
-grouped GEMM on small integers (plain and packed weights) equal to the bf16
-rounding of the exact sums."""
+the unit-weight combine of the dispatched rows equal to K_eff * x, the packed
+fp8 rows byte for byte (scale 2^-6 and payload codes of 64 * x), grouped rows,
+their row lists and the grouped-order combine, and the grouped GEMM on small
+integers (plain and packed weights) equal to the bf16 rounding of the exact
+sums."""
 import os
 import subprocess
 

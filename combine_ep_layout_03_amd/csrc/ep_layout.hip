@@ -134,6 +134,51 @@ __global__ __launch_bounds__(1024) void k_layout_colscan(int* __restrict__ parti
   }
 }
 
+// The same scan for 257 to 2048 rows: block = 16 columns x 64 row slices of
+// at most kScanRowsWide rows; the slice sums of a column are scanned in
+// log2(64) steps across the slices rather than one after another.
+constexpr int kScanColsWide = 16;
+constexpr int kScanSlicesWide = 64;
+constexpr int kScanRowsWide = 32;
+
+__global__ __launch_bounds__(1024) void k_layout_colscan_wide(int* __restrict__ partials,
+                                                              int nblocks, int ncols) {
+  __shared__ int s[kScanSlicesWide][kScanColsWide + 1];
+  const int cl = threadIdx.x % kScanColsWide;
+  const int rl = threadIdx.x / kScanColsWide;
+  const int c = blockIdx.x * kScanColsWide + cl;
+  const int chunk = (nblocks + kScanSlicesWide - 1) / kScanSlicesWide;
+  const int b0 = rl * chunk;
+  int v[kScanRowsWide];
+  int sum = 0;
+#pragma unroll
+  for (int j = 0; j < kScanRowsWide; ++j) {
+    const int b = b0 + j;
+    v[j] = (j < chunk && b < nblocks && c < ncols) ? partials[static_cast<size_t>(b) * ncols + c] : 0;
+    sum += v[j];
+  }
+  s[rl][cl] = sum;
+  __syncthreads();
+  // inclusive scan over the slices (Hillis-Steele), then this slice's base
+  for (int off = 1; off < kScanSlicesWide; off <<= 1) {
+    const int add = rl >= off ? s[rl - off][cl] : 0;
+    __syncthreads();
+    s[rl][cl] += add;
+    __syncthreads();
+  }
+  if (rl == kScanSlicesWide - 1 && c < ncols)
+    partials[static_cast<size_t>(nblocks) * ncols + c] = s[rl][cl];
+  int run = s[rl][cl] - sum;
+#pragma unroll
+  for (int j = 0; j < kScanRowsWide; ++j) {
+    const int b = b0 + j;
+    if (j < chunk && b < nblocks && c < ncols) {
+      partials[static_cast<size_t>(b) * ncols + c] = run;
+      run += v[j];
+    }
+  }
+}
+
 template <bool GROUPED>
 __global__ __launch_bounds__(kBlock) void k_layout_place(LayoutArgs a, int ncols, int rounds,
                                                          int nblocks) {
@@ -319,9 +364,13 @@ __global__ __launch_bounds__(kBlock) void k_layout_place(LayoutArgs a, int ncols
 
 LayoutGeom layout_geom(int64_t n_entries, int E, int G) {
   LayoutGeom g;
-  // at most 256 blocks (the column scan's limit, 16 * kScanRows), each
-  // thread taking `rounds` entries
-  const int64_t per_round = static_cast<int64_t>(kBlock) * 256;
+  // One entry per thread on up to 256 blocks (the narrow scan's limit,
+  // 16 * kScanRows); beyond that up to 2048 blocks (the wide scan's limit,
+  // kScanSlicesWide * kScanRowsWide), each thread taking `rounds` entries.
+  const int64_t max_blocks = n_entries <= static_cast<int64_t>(kBlock) * 16 * kScanRows
+                                 ? 16 * kScanRows
+                                 : kScanSlicesWide * kScanRowsWide;
+  const int64_t per_round = static_cast<int64_t>(kBlock) * max_blocks;
   int64_t rounds = (n_entries + per_round - 1) / per_round;
   if (rounds < 1) rounds = 1;
   g.rounds = static_cast<int>(rounds);
@@ -350,8 +399,12 @@ hipError_t launch_layout(const LayoutArgs& a, const LayoutGeom& geo, hipStream_t
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
 
-  k_layout_colscan<<<(geo.ncols + kWave - 1) / kWave, 1024, 0, s>>>(a.partials, geo.nblocks,
-                                                                    geo.ncols);
+  if (geo.nblocks <= 16 * kScanRows)
+    k_layout_colscan<<<(geo.ncols + kWave - 1) / kWave, 1024, 0, s>>>(a.partials, geo.nblocks,
+                                                                      geo.ncols);
+  else
+    k_layout_colscan_wide<<<(geo.ncols + kScanColsWide - 1) / kScanColsWide, 1024, 0, s>>>(
+        a.partials, geo.nblocks, geo.ncols);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
 

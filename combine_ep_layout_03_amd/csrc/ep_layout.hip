@@ -194,16 +194,31 @@ __global__ __launch_bounds__(kBlock) void k_layout_place(LayoutArgs a, int ncols
   const int wave = tid / kWave;
   const int lane = tid & (kWave - 1);
   const int* tot = a.partials + static_cast<size_t>(nblocks) * ncols;
+  const int* mine = a.partials + static_cast<size_t>(blockIdx.x) * ncols;
   const uint32_t base = blockIdx.x * static_cast<uint32_t>(rounds) * kBlock;
   // the first round's id, loaded early so its latency overlaps the scans
   int64_t v_next = (base + tid < a.n) ? a.idx[base + tid] : -1;
+  // this thread's keys' totals and this block's tallies, loaded together
+  // up front (keys tid, tid + kBlock, ...; at most EP_MAX_KEYS + 1 columns)
+  constexpr int kKeysPerThread = (1024 + kBlock - 1) / kBlock + 1;
+  int my_tot[kKeysPerThread], my_part[kKeysPerThread];
+#pragma unroll
+  for (int q = 0; q < kKeysPerThread; ++q) {
+    const int c = tid + q * kBlock;
+    my_tot[q] = c < nkeys ? tot[c] : 0;
+    my_part[q] = c < nkeys ? mine[c] : 0;
+  }
 
   // Segment bases: exclusive prefix sums over the experts of their counts
   // rounded up to the alignment, and (separately) over the groups.  The raw
   // expert counts are scanned too, for the number of selections.
   const int A = a.align;
-  for (int c = tid; c < E; c += kBlock) run[c] = tot[c];
-  for (int c = tid; c < nkeys; c += kBlock) sbase[c] = c < E ? (tot[c] + A - 1) / A * A : tot[c];
+#pragma unroll
+  for (int q = 0; q < kKeysPerThread; ++q) {
+    const int c = tid + q * kBlock;
+    if (c < E) run[c] = my_tot[q];
+    if (c < nkeys) sbase[c] = c < E ? (my_tot[q] + A - 1) / A * A : my_tot[q];
+  }
   __syncthreads();
   const int n_sel = A > 1 ? block_exclusive_scan(run, E, tmp) : 0;
   const int n_rows_e = block_exclusive_scan(sbase, E, tmp);
@@ -250,10 +265,13 @@ __global__ __launch_bounds__(kBlock) void k_layout_place(LayoutArgs a, int ncols
   __syncthreads();  // run[] is reused below
 
   // This block's base per key: segment base + entries of earlier blocks.
-  const int* mine = a.partials + static_cast<size_t>(blockIdx.x) * ncols;
-  for (int c = tid; c < nkeys; c += kBlock) {
-    sbase[c] += mine[c];
-    run[c] = 0;
+#pragma unroll
+  for (int q = 0; q < kKeysPerThread; ++q) {
+    const int c = tid + q * kBlock;
+    if (c < nkeys) {
+      sbase[c] += my_part[q];
+      run[c] = 0;
+    }
   }
   for (int c = tid; c < kWavesPerBlock * nkeys; c += kBlock) bm[c] = 0;
   __syncthreads();

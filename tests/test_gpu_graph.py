@@ -1,4 +1,5 @@
-"""The dispatch/combine step captured in a HIP graph (torch.cuda.graph).
+"""The dispatch/combine step, and the grouped path with the GEMM, captured
+in a HIP graph (torch.cuda.graph).
 
 The library only enqueues kernels on the caller's stream: it allocates,
 clears and synchronises nothing, so a step with preallocated outputs can be
@@ -95,3 +96,81 @@ def test_step_graph_replays_match_eager_and_oracle():
             got = recv[:n, :rb].cpu().numpy()
             want_rows = O.dispatch_fp8(xs, R["slot"], n)
             assert np.array_equal(got, want_rows)
+
+
+def test_grouped_step_graph_replays_match_eager_and_oracle():
+    """The grouped path captured once and replayed: grouped layout with row
+    lists and expert-row map (96,000 entries, past 65,536, so the wide column
+    scan runs), one bf16 row per (token, group hit), the grouped-order
+    combine, and the grouped GEMM gathering its rows from the token matrix
+    through packed weights.  Every replay, on new routing, weights and token
+    rows, equals an eager run on separate buffers bit for bit; the first is
+    also checked against the oracle (layout, group rows, grouped combine)."""
+    import combine_ep_layout_03_amd as ep
+
+    base = W.Workload("graph_grouped", T=12000, H=256, K=8, E=64, G=8, mask_p=0.05, seed=3)
+    T, H, K, E, G = base.T, base.H, base.K, base.E, base.G
+    N = 256
+    idx0, wt0 = W.make_routing(base)
+    d_idx, d_wt = idx0.to(DEV), wt0.to(DEV)
+    x = W.make_x(base, device=DEV)
+    y = W.make_y(base, device=DEV)
+    packed = ep.ep_pack_expert_weights(W.make_expert_weights(base, N).to(DEV))
+
+    def buffers():
+        Lx = ep.ep_layout(d_idx, E, G, d_wt, expert_row_src=True)
+        return (
+            Lx,
+            torch.full((Lx.max_group_rows(), H), 7.0, dtype=torch.bfloat16, device=DEV),
+            torch.empty(T, H, dtype=torch.bfloat16, device=DEV),
+            torch.zeros(Lx.max_expert_rows(), N, dtype=torch.bfloat16, device=DEV),
+        )
+
+    def step(Lx, rx, ox, gx):
+        ep.ep_layout(d_idx, E, G, d_wt, out=Lx)
+        ep.ep_dispatch(x, Lx, rows=ep.EP_ROWS_GROUP, out=rx)
+        ep.ep_combine(y, Lx, d_wt, d_idx, order=ep.EP_COMBINE_GROUPED, out=ox)
+        ep.ep_expert_gemm(x, Lx, packed, out=gx, gather=True)
+
+    L, recv, out, yg = buffers()
+    Le, recv_e, out_e, yg_e = buffers()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(L, recv, out, yg)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(L, recv, out, yg)
+    torch.cuda.synchronize()
+
+    for rep in range(4):
+        w = base.replace(seed=200 + rep)
+        idx, wt = W.make_routing(w)
+        d_idx.copy_(idx.to(DEV))
+        d_wt.copy_(wt.to(DEV))
+        x.copy_(W.make_x(w, device=DEV))
+        torch.cuda.synchronize()
+        step(Le, recv_e, out_e, yg_e)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name in ("counts", "offsets", "slot", "grow", "group_counts", "group_offsets", "expert_row_src"):
+            assert torch.equal(getattr(L, name), getattr(Le, name)), f"replay {rep}: {name}"
+        ng = int(L.status[2].item())
+        ne = int(L.status[1].item())
+        assert ng == int(Le.status[2].item()) and ne == int(Le.status[1].item())
+        for name in ("row_src", "row_topk_idx"):
+            assert torch.equal(getattr(L, name)[:ng], getattr(Le, name)[:ng]), f"replay {rep}: {name}"
+        assert torch.equal(L.row_topk_weights[:ng].view(torch.int32), Le.row_topk_weights[:ng].view(torch.int32))
+        assert torch.equal(recv[:ng].view(torch.int16), recv_e[:ng].view(torch.int16)), f"replay {rep}: group rows"
+        assert torch.equal(out.view(torch.int16), out_e.view(torch.int16)), f"replay {rep}: grouped combine"
+        assert torch.equal(yg[:ne].view(torch.int16), yg_e[:ne].view(torch.int16)), f"replay {rep}: gemm"
+        if rep == 0:
+            R = O.layout(idx.numpy(), E, G, wt.numpy())
+            assert np.array_equal(L.grow.cpu().numpy(), R["grow"])
+            assert np.array_equal(L.slot.cpu().numpy(), R["slot"])
+            assert np.array_equal(u16(recv[:ng]), O.dispatch_bf16(u16(x), R["grow"], R["n_rows"]))
+            want = O.combine_grouped(u16(y), idx.numpy(), R["slot"], wt.numpy(), E, G)
+            assert np.array_equal(u16(out), want)

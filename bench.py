@@ -58,7 +58,7 @@ def counted_traffic(op, workload):
     return rec.get("bytes_per_launch")
 
 
-def time_extras(ep, W, w, d_idx, d_wt, x, y, L, n_sel, rb, pitch, reps, only=None):
+def time_extras(ep, W, w, d_idx, d_wt, x, y, L, n_sel, rb, pitch, reps, only=None, flush=None):
     """Each op beside the headline step, timed alone (back to back, HIP
     events on the current stream) at the same 8192 x 7168 workload:
     grouped-order combine over 8 groups of 32 experts, the grouped (deduped)
@@ -66,11 +66,15 @@ def time_extras(ep, W, w, d_idx, d_wt, x, y, L, n_sel, rb, pitch, reps, only=Non
     padding, combine seeded by two bias rows, and the layout with
     receive-stats accumulation, the grouped GEMM consumer (plain weights,
     packed weights, and fused with the dispatch), the skewed and
-    masked routing, and one GPU's grouped receive share at 65,536 tokens.
-    ``only``, if given, names the cases to run."""
+    masked routing, and one GPU's grouped receive share at 65,536 tokens;
+    also the fp8 dispatch at the packed 7392-byte pitch and the tiny and mid
+    configurations, warm and with cold caches (``flush`` runs before each
+    cold call).  ``only``, if given, names the cases to run."""
     import torch
 
     dev = x.device
+    if flush is None:
+        flush = CacheFlush(dev)
     T, H, K, E = w.T, w.H, w.K, w.E
     stream = torch.cuda.current_stream(dev)
     G = 8
@@ -211,6 +215,22 @@ def time_extras(ep, W, w, d_idx, d_wt, x, y, L, n_sel, rb, pitch, reps, only=Non
             }
             del recv16, Lf
         del wts, yg
+    if want("dispatch_fp8_packed_pitch"):
+        # the packed fp8 rows back to back (7392-byte pitch at hidden 7168),
+        # the PR's own row, against the 128-byte aligned pitch of the step
+        recv_p = torch.empty(T * K, rb, dtype=torch.uint8, device=dev)
+        fn = lambda: ep.ep_dispatch(x, L, fp8=True, out=recv_p)  # noqa: E731
+        nbytes = T * H * 2 + T * K * 4 + n_sel * rb
+        res["dispatch_fp8_packed_pitch"] = {
+            "row_bytes": int(rb),
+            "warm": us_stats(per_call_us(fn, reps, stream), nbytes),
+            "cold": us_stats(per_call_us(fn, reps, stream, before=flush), nbytes),
+        }
+        del recv_p
+    if want("tiny"):
+        res["tiny"] = time_tiny(ep, W, dev, stream, reps)
+    if want("mid"):
+        res["mid"] = time_mid(ep, W, dev, stream, reps, flush)
     if want("grouped_t65536_g8"):
         res["grouped_t65536_g8"] = time_grouped_receive_share(ep, W, dev, stream, gemm_reps)
     if want("skewed_masked"):
@@ -220,6 +240,114 @@ def time_extras(ep, W, w, d_idx, d_wt, x, y, L, n_sel, rb, pitch, reps, only=Non
         f"(of which {n_al - n_sel} padding, counted as written bytes)"
     )
     ep.ep_layout(d_idx, E, out=L)  # restore the headline layout
+    return res
+
+
+class CacheFlush:
+    """Reads a 1 GiB buffer, which evicts whatever the next op reads from L2
+    and from the 256 MB memory-side cache without leaving dirty lines to be
+    written back during that op (a write flush was measured to time its own
+    write-back instead)."""
+
+    def __init__(self, dev):
+        import torch
+
+        self.buf = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+        self.sink = torch.zeros((), dtype=torch.int64, device=dev)
+
+    def __call__(self):
+        self.sink += self.buf.sum()
+
+
+def per_call_us(fn, reps, stream, before=None):
+    """Each of `reps` calls of `fn` bracketed by its own HIP events on
+    `stream` (the stream the kernels run on); `before`, if given, runs
+    untimed ahead of every call.  Returns the sorted durations in us."""
+    import torch
+
+    fn()
+    torch.cuda.synchronize()
+    marks = []
+    for _ in range(reps):
+        if before is not None:
+            before()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        marks.append((a, b))
+    torch.cuda.synchronize()
+    return sorted(a.elapsed_time(b) * 1e3 for a, b in marks)
+
+
+def us_stats(v, nbytes=None):
+    med = statistics.median(v)
+    out = {"us_median": round(med, 2), "us_min": round(min(v), 2), "us_max": round(max(v), 2)}
+    if nbytes is not None:
+        out.update({
+            "bytes": int(nbytes),
+            "GBps": round(nbytes / (med * 1e-6) / 1e9, 1),
+            "pct_of_peak": round(100.0 * nbytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
+        })
+    return out
+
+
+def time_tiny(ep, W, dev, stream, reps):
+    """The tiny configuration (128 tokens x 256, top-2 of 16 experts, expert
+    outputs = dispatched rows x (1 + e/16)): layout, bf16 dispatch and
+    combine, each call timed on its own.  Latency-bound (0.2 MB per op), so
+    only microseconds are reported."""
+    import torch
+
+    w = W.by_name("tiny")
+    idx, wt = W.make_routing(w)
+    d_idx, d_wt = idx.to(dev), wt.to(dev)
+    x = W.make_x(w, device=dev)
+    L = ep.ep_layout(d_idx, w.E)
+    n_sel = L.num_rows()
+    recv = ep.ep_dispatch(x, L)
+    row_expert = torch.repeat_interleave(torch.arange(w.E, device=dev), L.counts.long())
+    y = W.tiny_expert_outputs(recv[:n_sel], row_expert)
+    out = torch.empty(w.T, w.H, dtype=torch.bfloat16, device=dev)
+    res = {"selections": int(n_sel)}
+    for name, fn in (
+        ("layout", lambda: ep.ep_layout(d_idx, w.E, out=L)),
+        ("dispatch_bf16", lambda: ep.ep_dispatch(x, L, out=recv)),
+        ("combine", lambda: ep.ep_combine(y, L, d_wt, out=out)),
+    ):
+        res[name] = us_stats(per_call_us(fn, reps, stream))
+    return res
+
+
+def time_mid(ep, W, dev, stream, reps, flush):
+    """The mid configuration (4096 tokens x 4096, top-4 of 64 experts,
+    uniform): bf16 dispatch and combine, each call timed on its own, warm and
+    with cold caches.  Both ops' working sets (about 168 MB) fit the 256 MB
+    memory-side cache, so only the cold figure measures HBM."""
+    import torch
+
+    w = W.by_name("mid")
+    T, H, K, E = w.T, w.H, w.K, w.E
+    idx, wt = W.make_routing(w)
+    d_idx, d_wt = idx.to(dev), wt.to(dev)
+    x = W.make_x(w, device=dev)
+    y = W.make_y(w, device=dev)
+    L = ep.ep_layout(d_idx, E)
+    n_sel = L.num_rows()
+    recv = torch.empty(n_sel, H, dtype=torch.bfloat16, device=dev)
+    out = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    nb = algorithmic_bytes(T, H, K, E, n_sel, 0)
+    res = {"selections": int(n_sel)}
+    for name, fn, nbytes in (
+        ("dispatch_bf16", lambda: ep.ep_dispatch(x, L, out=recv, capacity=n_sel), nb["dispatch_bf16"]),
+        ("combine", lambda: ep.ep_combine(y, L, d_wt, out=out), nb["combine"]),
+    ):
+        res[name] = {
+            "warm": us_stats(per_call_us(fn, reps, stream), nbytes),
+            "cold": us_stats(per_call_us(fn, reps, stream, before=flush), nbytes),
+        }
+    del x, y, recv, out
     return res
 
 
@@ -581,18 +709,16 @@ def main(argv=None):
         del graph
 
     ev_cold = {k: [] for k in ev}
+    flush = CacheFlush(dev)
     if not args.no_cold:
         # cold caches: read 1 GiB before every step (outside the timed
         # events), which evicts the step's inputs from L2 and the 256 MB
         # memory-side cache without leaving dirty lines to write back during
         # the step
-        scratch = torch.ones(1 << 28, dtype=torch.int32, device=dev)
-        sink = torch.zeros((), dtype=torch.int64, device=dev)
         for _ in range(args.steps):
-            sink += scratch.sum()
+            flush()
             step(True, ev_cold)
         torch.cuda.synchronize()
-        del scratch, sink
         print("# cold-cache pass done", file=sys.stderr, flush=True)
 
     def ms(a, b, evd=ev):
@@ -665,7 +791,9 @@ def main(argv=None):
             ops[name]["isolated_us"] = round(us, 2)
             ops[name]["isolated_GBps"] = round(ops[name]["bytes"] / (us * 1e-6) / 1e9, 1)
     only = None if args.extras is None else set(s for s in args.extras.split(",") if s)
-    extras = {} if args.no_extras else time_extras(ep, W, w, d_idx, d_wt, x, y, L, n_sel, rb, pitch, args.steps, only)
+    extras = {} if args.no_extras else time_extras(ep, W, w, d_idx, d_wt, x, y, L, n_sel, rb, pitch, args.steps,
+                                                   only, flush)
+    del flush
     step_bytes = nb["layout"] + nb["dispatch_fp8"] + nb["combine"]
     step_ms = statistics.median(t_step)
     value = step_bytes / (step_ms * 1e-3) / 1e9
@@ -713,6 +841,19 @@ def main(argv=None):
             "avg_launch_us": round(avg_us, 2),
         },
     }
+    if ops_cold is not None:
+        # The >= 60%-of-HBM target is judged on the cold-cache figures: with
+        # warm caches the fp8 dispatch reads its 117 MB of token rows from the
+        # memory-side cache (a rate that in a model's forward pass, where the
+        # previous layer just wrote those rows, is the realistic one, but not
+        # an HBM rate).  The combine reads 940 MB, far more than that cache,
+        # so its warm and cold figures agree.
+        res["hbm_target_60pct"] = {
+            "basis": "cold caches: a 1 GiB read before each step evicts L2 and the 256 MB memory-side cache",
+            "pct_of_peak": {k: ops_cold[k]["pct_of_peak"] for k in ("dispatch_fp8", "dispatch_e2e", "combine")},
+            "warm_is_cache_assisted": {k: ops[k]["pct_of_peak"] for k in ("dispatch_fp8", "dispatch_e2e")},
+            "met": all(ops_cold[k]["pct_of_peak"] >= 60.0 for k in ("dispatch_fp8", "dispatch_e2e", "combine")),
+        }
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         x_host = x.cpu().view(torch.int16).numpy().view(np.uint16)

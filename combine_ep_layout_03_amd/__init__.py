@@ -23,7 +23,10 @@ from ._lib import (  # noqa: F401
     EP_ROWS_EXPERT,
     EP_ROWS_GROUP,
     EP_STATUS_COMBINE_OOB,
+    EP_STATUS_DISPATCH_OVERFLOW,
     EP_STATUS_EXPERT_LIST_OVERFLOW,
+    EP_STATUS_GENERATION,
+    EP_STATUS_STALE,
     EP_STATUS_INVALID_IDS,
     EP_STATUS_SELECTIONS,
     EP_STATUS_LIST_OVERFLOW,
@@ -107,10 +110,14 @@ class StaleLayoutError(RuntimeError):
 class Layout:
     """Device outputs of ep_layout plus the shape they were computed for.
 
-    ``generation`` counts the ep_layout calls that wrote these buffers; a
+    ``generation`` is the value the library's ep_layout stamped on these
+    buffers (unique in the process, 0 before the first layout).  A
     LayoutHandle taken with ``handle()`` remembers it, so a dispatch replayed
     from a cached handle is rejected once the buffers hold another routing
-    (the PR's cached ``handle=`` dispatch and its stale-layout guard)."""
+    (the PR's cached ``handle=`` dispatch and its stale-layout guard): on the
+    host by ``LayoutHandle.get()``, and on the device by the kernels, which
+    compare the handle's generation with the one stamped in the status words
+    and write nothing on a mismatch (so a replayed HIP graph is guarded too)."""
 
     num_tokens: int
     topk: int
@@ -134,7 +141,9 @@ class Layout:
     recv_stats: torch.Tensor | None = None
     generation: int = 0
 
-    def struct(self) -> _lib.LayoutStruct:
+    def struct(self, generation: int | None = None) -> _lib.LayoutStruct:
+        """The C struct over these buffers, carrying ``generation`` (default:
+        the buffers' current one) for the kernels' stale-layout check."""
         return _lib.LayoutStruct(
             _ptr(self.counts),
             _ptr(self.offsets),
@@ -150,6 +159,7 @@ class Layout:
             _ptr(self.expert_row_src),
             self.expert_row_capacity,
             _ptr(self.recv_stats),
+            self.generation if generation is None else int(generation),
         )
 
     def max_expert_rows(self) -> int:
@@ -166,6 +176,20 @@ class Layout:
 
     def handle(self) -> "LayoutHandle":
         return LayoutHandle(self, self.generation)
+
+    def status_word(self, word: int) -> int:
+        """One device status word (synchronises the stream)."""
+        return int(self.status[word].item())
+
+    def dispatch_overflowed(self) -> bool:
+        """Whether the last ep_dispatch on this layout needed more rows than
+        its capacity (it then wrote no row).  Synchronises."""
+        return self.status_word(EP_STATUS_DISPATCH_OVERFLOW) != 0
+
+    def stale_call_seen(self) -> bool:
+        """Whether a call since the last ep_layout was handed a stale
+        generation (it then wrote nothing).  Synchronises."""
+        return self.status_word(EP_STATUS_STALE) != 0
 
 
 @dataclasses.dataclass(frozen=True)
@@ -184,8 +208,11 @@ class LayoutHandle:
         return self.layout
 
 
-def _resolve(layout) -> Layout:
-    return layout.get() if isinstance(layout, LayoutHandle) else layout
+def _resolve(layout) -> tuple[Layout, int]:
+    """The Layout and the generation a call on it must carry."""
+    if isinstance(layout, LayoutHandle):
+        return layout.get(), layout.generation
+    return layout, layout.generation
 
 
 def ep_layout(
@@ -283,7 +310,7 @@ def _run_layout(L: Layout, topk_idx: torch.Tensor, topk_weights: torch.Tensor | 
         _stream(topk_idx.device),
     )
     _lib.check("ep_layout", rc)
-    L.generation += 1
+    L.generation = int(s.generation)
 
 
 def ep_dispatch(
@@ -295,6 +322,7 @@ def ep_dispatch(
     out: torch.Tensor | None = None,
     row_stride: int | None = None,
     zero_padding: bool = False,
+    check: bool = False,
 ) -> torch.Tensor:
     """Scatter token rows x (bf16 [T, H]) to their receive rows.
 
@@ -304,10 +332,14 @@ def ep_dispatch(
     ``row_stride`` bytes (default: the row size, rows packed back to back).
     Only the first row-size bytes of each row are written.  The default
     capacity is the worst case (T*K expert rows, min(T*G, T*K) group rows),
-    so no host synchronisation is needed.  ``layout`` may be a LayoutHandle
-    (checked against its generation).  ``zero_padding`` also zeroes the
-    expert alignment padding rows."""
-    layout = _resolve(layout)
+    so no host synchronisation is needed.  With a smaller ``capacity`` the
+    rows needed may exceed it: the call then writes no row and sets the
+    status word EP_STATUS_DISPATCH_OVERFLOW (``layout.dispatch_overflowed()``;
+    ``check=True`` synchronises and raises EPError instead).  ``layout`` may
+    be a LayoutHandle (checked against its generation, on the host and on
+    the device).  ``zero_padding`` also zeroes the expert alignment padding
+    rows."""
+    layout, gen = _resolve(layout)
     if x.dim() != 2 or x.shape[0] != layout.num_tokens:
         raise ValueError("x must be [T, H] with the layout's T")
     _dev(x, "x", torch.bfloat16)
@@ -337,7 +369,7 @@ def ep_dispatch(
     pitch = out.shape[1] * esize
     flags = _lib.EP_FLAG_ZERO_PADDING if zero_padding else 0
     p = _problem(T, H, layout.topk, layout.num_experts, layout.num_groups, layout.expert_alignment, flags)
-    s = layout.struct()
+    s = layout.struct(gen)
     rc = _lib.lib().ep_dispatch(
         ctypes.byref(p),
         ctypes.byref(s),
@@ -350,6 +382,13 @@ def ep_dispatch(
         _stream(x.device),
     )
     _lib.check("ep_dispatch", rc)
+    if check and T > 0:
+        if layout.stale_call_seen():
+            raise StaleLayoutError("the layout buffers were recomputed before this dispatch ran")
+        if layout.dispatch_overflowed():
+            need = layout.num_rows(rows)
+            raise _lib.EPError("ep_dispatch", _lib.EP_EINVAL,
+                               f"{need} receive rows needed, capacity {capacity}: nothing written")
     return out
 
 
@@ -366,7 +405,7 @@ def ep_combine(
     """Weighted reduction of each token's expert-output rows y (bf16 [rows, H],
     expert-major) into out (bf16 [T, H]); bias0 / bias1 (bf16 [T, H]) seed the
     accumulator."""
-    layout = _resolve(layout)
+    layout, gen = _resolve(layout)
     if y.dim() != 2:
         raise ValueError("y must be [rows, H]")
     _dev(y, "y", torch.bfloat16)
@@ -385,7 +424,7 @@ def ep_combine(
     else:
         _dev(out, "out", torch.bfloat16, (T, H))
     p = _problem(T, H, K, layout.num_experts, layout.num_groups, layout.expert_alignment)
-    s = layout.struct()
+    s = layout.struct(gen)
     rc = _lib.lib().ep_combine(
         ctypes.byref(p),
         ctypes.byref(s),
@@ -452,7 +491,7 @@ def ep_expert_gemm(
     with ``gather``, row expert_row_src[r] of the token matrix x (bf16
     [T, >= H]): the dispatch folded into the GEMM's loads, which needs a
     layout computed with ``expert_row_src=True``."""
-    layout = _resolve(layout)
+    layout, gen = _resolve(layout)
     packed = isinstance(w, PackedExpertWeights)
     if packed:
         E, N, H = w.num_experts, w.n_out, w.hidden
@@ -490,7 +529,7 @@ def ep_expert_gemm(
     flags = (_lib.EP_FLAG_GATHER_ROWS if gather else 0) | (_lib.EP_FLAG_PACKED_WEIGHTS if packed else 0)
     p = _problem(layout.num_tokens, H, layout.topk, layout.num_experts, layout.num_groups,
                  layout.expert_alignment, flags)
-    s = layout.struct()
+    s = layout.struct(gen)
     rc = _lib.lib().ep_expert_gemm(
         ctypes.byref(p), ctypes.byref(s), _ptr(x), int(x.shape[1]), _ptr(wt), int(N), _ptr(out), int(out.shape[1]),
         _stream(x.device),

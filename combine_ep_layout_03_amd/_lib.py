@@ -28,7 +28,10 @@ EP_STATUS_LIST_OVERFLOW = 3
 EP_STATUS_COMBINE_OOB = 4
 EP_STATUS_EXPERT_LIST_OVERFLOW = 5
 EP_STATUS_SELECTIONS = 6
-EP_STATUS_WORDS = 8
+EP_STATUS_DISPATCH_OVERFLOW = 7
+EP_STATUS_GENERATION = 8
+EP_STATUS_STALE = 9
+EP_STATUS_WORDS = 16
 
 EP_FLAG_ZERO_PADDING = 1
 EP_FLAG_GATHER_ROWS = 2
@@ -82,6 +85,7 @@ class LayoutStruct(ctypes.Structure):
         ("expert_row_src", ctypes.c_void_p),
         ("expert_row_capacity", ctypes.c_int64),
         ("recv_stats", ctypes.c_void_p),
+        ("generation", ctypes.c_uint32),
     ]
 
 

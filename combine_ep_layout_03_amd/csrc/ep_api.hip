@@ -3,10 +3,28 @@
 #include <limits.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "ep_internal.h"
 #include "ep_mi355x.h"
 
 namespace {
+
+static_assert(EP_STATUS_DISPATCH_OVERFLOW == ep::kStatusDispatchOverflow &&
+                  EP_STATUS_GENERATION == ep::kStatusGeneration &&
+                  EP_STATUS_STALE == ep::kStatusStale && EP_STATUS_WORDS == 16,
+              "status word numbering");
+
+// Layout generations, unique in the process (never 0, so a zeroed
+// ep_layout_t that no ep_layout has stamped never matches).
+uint32_t next_generation() {
+  static std::atomic<uint32_t> counter{0};
+  uint32_t g;
+  do {
+    g = counter.fetch_add(1, std::memory_order_relaxed) + 1;
+  } while (g == 0);
+  return g;
+}
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -53,8 +71,7 @@ size_t ep_layout_workspace_bytes(const ep_problem_t* p) {
 }
 
 int ep_layout(const ep_problem_t* p, const int64_t* topk_idx, const float* topk_weights,
-              const ep_layout_t* L, void* workspace, size_t workspace_bytes,
-              hipStream_t stream) {
+              ep_layout_t* L, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   int rc = check_problem(p);
   if (rc != EP_OK) return rc;
   if (!L || !L->counts || !L->offsets || !L->status || !workspace) return EP_EINVAL;
@@ -98,7 +115,10 @@ int ep_layout(const ep_problem_t* p, const int64_t* topk_idx, const float* topk_
   a.expert_row_cap = L->expert_row_src ? L->expert_row_capacity : 0;
   a.recv_stats = L->recv_stats;
   a.partials = static_cast<int32_t*>(workspace);
-  return ep::launch_layout(a, g, stream) == hipSuccess ? EP_OK : EP_EHIP;
+  a.generation = next_generation();
+  if (ep::launch_layout(a, g, stream) != hipSuccess) return EP_EHIP;
+  L->generation = a.generation;
+  return EP_OK;
 }
 
 int ep_dispatch(const ep_problem_t* p, const ep_layout_t* L, const void* x, void* recv,
@@ -127,6 +147,8 @@ int ep_dispatch(const ep_problem_t* p, const ep_layout_t* L, const void* x, void
   a.recv = recv;
   a.dest = dest;
   a.rows_needed = L->status + (rows == EP_ROWS_EXPERT ? EP_STATUS_ROWS_EXPERT : EP_STATUS_ROWS_GROUP);
+  a.status = L->status;
+  a.generation = L->generation;
   a.T = p->num_tokens;
   a.K = p->topk;
   a.H = p->hidden;
@@ -184,6 +206,7 @@ int ep_combine(const ep_problem_t* p, const ep_layout_t* L, const int64_t* topk_
   a.bias1 = bias1;
   a.out = out;
   a.status = L->status;
+  a.generation = L->generation;
   a.grouped = grouped;
   int ve = vec_bytes_for(static_cast<int64_t>(p->hidden) * 2, y ? y : out, out) / 2;
   while (ve > 1 && (!aligned(bias0, 2 * ve) || !aligned(bias1, 2 * ve))) ve >>= 1;
@@ -195,7 +218,8 @@ int ep_expert_gemm(const ep_problem_t* p, const ep_layout_t* L, const void* x,
                    int64_t y_row_stride, hipStream_t stream) {
   int rc = check_problem(p);
   if (rc != EP_OK) return rc;
-  if (!L || !L->counts || !L->offsets || x_row_stride < 0 || y_row_stride < 0 || n_out < 1)
+  if (!L || !L->counts || !L->offsets || !L->status || x_row_stride < 0 || y_row_stride < 0 ||
+      n_out < 1)
     return EP_EINVAL;
   if (p->hidden % 64 != 0 || n_out % 128 != 0) return EP_ENOTSUP;
   const int64_t ldx = x_row_stride == 0 ? p->hidden : x_row_stride;
@@ -215,6 +239,8 @@ int ep_expert_gemm(const ep_problem_t* p, const ep_layout_t* L, const void* x,
   a.H = p->hidden;
   a.N = n_out;
   a.ntn = (n_out + 255) / 256;
+  a.status = L->status;
+  a.generation = L->generation;
   const int64_t pad = static_cast<int64_t>(p->num_experts) *
                       (p->expert_alignment > 1 ? p->expert_alignment - 1 : 0);
   const int64_t max_rows = p->num_tokens * p->topk + pad;

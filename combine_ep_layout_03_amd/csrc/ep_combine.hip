@@ -233,6 +233,7 @@ template <int KMAX, int VE, bool GROUPED, int U, int NB>
 __global__ __launch_bounds__(kBlock) void k_combine(CombineArgs a, int nchunks, int64_t items) {
   using B = BfVec<VE>;
   using V = typename B::V;
+  if (!layout_current(a.status, a.generation)) return;  // stale handle: write nothing
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t nw = grid_waves();
   const int nvec = a.H / VE;

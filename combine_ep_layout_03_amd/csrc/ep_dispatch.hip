@@ -1,8 +1,9 @@
 // Dispatch: scatter each token row straight to its final receive rows.
 //
-// TileScale PR #68 ("EP v2 intranode dispatch/combine") writes every row at
-// send_base[d] + slot, its final compact index, so there is no copy
-// epilogue (PR summary; Design section).  Here a token row is cut into
+// Each row is stored once, at the expert-major destination the layout gave
+// it (base of its destination + claimed slot), so no compaction pass runs
+// afterwards (TileScale PR #68, "EP v2 intranode dispatch/combine": PR
+// summary and Design section).  Here a token row is cut into
 // chunks; the grid's waves take the (token, chunk) items cyclically, read
 // each chunk of the source row once and store it once per destination row.  Receive rows are written with non-temporal stores: they
 // are not read again by this step and streaming them past the caches
@@ -54,7 +55,7 @@ template <int KMAX, int VB, int U>
 __global__ __launch_bounds__(kBlock) void k_scatter_bf16(ScatterArgs a, int nchunks,
                                                          int64_t items) {
   using V = typename VecOf<VB>::type;
-  if (static_cast<int64_t>(*a.rows_needed) > a.capacity) return;  // overflow: write nothing
+  if (!dispatch_may_write(a)) return;  // stale layout or overflow: write nothing
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t nw = grid_waves();
   const int64_t row_bytes = static_cast<int64_t>(a.H) * 2;
@@ -115,7 +116,7 @@ template <int KMAX, bool ROWBUF>
 __global__ __launch_bounds__(kBlock) void k_scatter_fp8(ScatterArgs a, int64_t row_bytes) {
   constexpr int kMaxScaleSlots = 4;  // H <= 4 * 64 * 128
   constexpr int kRowSteps = 8;       // ROWBUF: H <= 8 * 1024
-  if (static_cast<int64_t>(*a.rows_needed) > a.capacity) return;
+  if (!dispatch_may_write(a)) return;
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t nw = grid_waves();
   int64_t t = global_wave();
@@ -235,7 +236,7 @@ __global__ __launch_bounds__(kBlock) void k_scatter_fp8(ScatterArgs a, int64_t r
 template <int VB>
 __global__ __launch_bounds__(kBlock) void k_zero_padding(ScatterArgs a, int64_t row_bytes) {
   using V = typename VecOf<VB>::type;
-  if (static_cast<int64_t>(*a.rows_needed) > a.capacity) return;
+  if (!dispatch_may_write(a)) return;
   const int nvec = static_cast<int>(row_bytes / VB);
   char* rbase = static_cast<char*>(a.recv);
   for (int e = blockIdx.x; e < a.E; e += gridDim.x) {

@@ -119,6 +119,8 @@ __global__ __launch_bounds__(kThreads) void k_expert_gemm(GemmArgs a) {
   int* const sTiles = reinterpret_cast<int*>(sW);
   int* const sTmp = sTiles + 1024 + 16;
 
+  // a stale layout handle: the whole grid returns before any barrier
+  if (!layout_current(a.status, a.generation)) return;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   // wave-uniform for the compiler too, so branches on it are scalar

@@ -39,14 +39,34 @@ struct LayoutArgs {
   int64_t expert_row_cap;
   uint32_t* recv_stats;  // optional, accumulated
   int32_t* partials;  // workspace
+  uint32_t generation;  // stamped into status[EP_STATUS_GENERATION]
 };
 hipError_t launch_layout(const LayoutArgs& a, const LayoutGeom& g, hipStream_t s);
+
+// Stale-layout guard shared by dispatch, combine and the GEMM: the kernels
+// run only if the layout buffers still carry the generation the caller's
+// handle was taken at (device word status[kStatusGeneration]); otherwise
+// they write nothing and set status[kStatusStale].
+constexpr int kStatusDispatchOverflow = 7;
+constexpr int kStatusGeneration = 8;
+constexpr int kStatusStale = 9;
+
+// Is the layout behind `status` still the one the caller's handle names?
+// Wave-uniform (one word, read by every lane).  On a stale handle the grid's
+// first lane sets the sticky stale flag; the caller's kernel then returns.
+__device__ __forceinline__ bool layout_current(int32_t* status, uint32_t generation) {
+  const bool cur = static_cast<uint32_t>(status[kStatusGeneration]) == generation;
+  if (!cur && blockIdx.x == 0 && threadIdx.x == 0) status[kStatusStale] = 1;
+  return cur;
+}
 
 struct ScatterArgs {
   const void* x;
   void* recv;
   const int32_t* dest;  // [T*K] slot or grow
   const int32_t* rows_needed;  // device word
+  int32_t* status;             // layout status words
+  uint32_t generation;         // the caller's handle
   int64_t T;
   int K;
   int H;
@@ -61,6 +81,16 @@ struct ScatterArgs {
 // bf16 rows; `vec_bytes` in {16, 8, 4, 2} divides the row size, the stride
 // and both base alignments.
 hipError_t launch_scatter_bf16(const ScatterArgs& a, int vec_bytes, hipStream_t s);
+
+// May a dispatch kernel write?  Only if the layout is current and its rows
+// fit the capacity (an overflow writes no row).  The grid's first lane
+// records the overflow verdict of a current call (1 or 0).
+__device__ __forceinline__ bool dispatch_may_write(const ScatterArgs& a) {
+  if (!layout_current(a.status, a.generation)) return false;
+  const bool fits = static_cast<int64_t>(*a.rows_needed) <= a.capacity;
+  if (blockIdx.x == 0 && threadIdx.x == 0) a.status[kStatusDispatchOverflow] = fits ? 0 : 1;
+  return fits;
+}
 // packed fp8 rows; H % 128 == 0, H <= 32768, 16-byte aligned bases and stride.
 hipError_t launch_scatter_fp8(const ScatterArgs& a, int64_t row_bytes, hipStream_t s);
 // zero the first row_bytes bytes of every alignment padding row; `vec_bytes`
@@ -83,6 +113,7 @@ struct CombineArgs {
   const void* bias1;  // optional bf16 [T*H]
   void* out;
   int32_t* status;
+  uint32_t generation;
   bool grouped;
 };
 // `vec_elems` in {8, 4, 2, 1} divides H and both base alignments (in bf16 elements).
@@ -105,6 +136,8 @@ struct GemmArgs {
   // (expert, column tile, 32-wide reduction step) block 16 KiB contiguous,
   // rows past N zero
   bool packed;
+  int32_t* status;
+  uint32_t generation;
 };
 // H % 64 == 0, N % 128 == 0, E <= 1024, 16-byte aligned x / w / y and strides
 // (ldx % 8 == 0, ldy % 4 == 0); max_rows bounds the expert-major rows.

@@ -250,7 +250,10 @@ __global__ __launch_bounds__(kBlock) void k_layout_place(LayoutArgs a, int ncols
       a.status[4] = 0;
       a.status[5] = (a.expert_row_src != nullptr && !erows_ok) ? 1 : 0;
       a.status[6] = A > 1 ? n_sel : n_rows_e;
-      a.status[7] = 0;
+      a.status[kStatusDispatchOverflow] = 0;
+      a.status[kStatusGeneration] = static_cast<int32_t>(a.generation);
+      a.status[kStatusStale] = 0;
+      for (int w = kStatusStale + 1; w < 16; ++w) a.status[w] = 0;
     }
   }
   // alignment padding rows are marked unoccupied (-1); experts are spread

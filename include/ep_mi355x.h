@@ -58,7 +58,12 @@ extern "C" {
 #define EP_MAX_TOPK 32     /* K */
 #define EP_MAX_KEYS 1024   /* E + G (destinations counted by the layout) */
 
-/* ---- device status words written by ep_layout ------------------------ */
+/* ---- device status words ---------------------------------------------
+ * ep_layout writes every word (words 4, 7 and 9 as 0); the other calls
+ * write only the words named here.  Data-dependent conditions are reported
+ * here rather than by corrupting memory, as the PR's expanded dispatch
+ * reports expand_overflow before any payload moves (commit adding DeepEP's
+ * do_expand). */
 #define EP_STATUS_INVALID_IDS 0 /* ids outside {-1} U [0,E): counted, treated as -1 */
 #define EP_STATUS_ROWS_EXPERT 1 /* rows of the expert-major layout (selections + padding) */
 #define EP_STATUS_ROWS_GROUP 2  /* R: rows of the grouped layout (0 without groups) */
@@ -66,7 +71,15 @@ extern "C" {
 #define EP_STATUS_COMBINE_OOB 4 /* set to 1 by ep_combine if a slot >= y_rows was met */
 #define EP_STATUS_EXPERT_LIST_OVERFLOW 5 /* 1 if expert rows > expert_row_capacity */
 #define EP_STATUS_SELECTIONS 6  /* valid selections (EP_STATUS_ROWS_EXPERT minus padding) */
-#define EP_STATUS_WORDS 8
+#define EP_STATUS_DISPATCH_OVERFLOW 7 /* written by every ep_dispatch: 1 if the rows it
+                                       * needed exceeded capacity_rows (it then wrote no
+                                       * row), else 0 */
+#define EP_STATUS_GENERATION 8  /* the generation ep_layout stamped on these buffers */
+#define EP_STATUS_STALE 9       /* set to 1 (sticky until the next ep_layout) by a
+                                 * dispatch, combine or GEMM handed an ep_layout_t whose
+                                 * generation is not EP_STATUS_GENERATION; that call
+                                 * wrote nothing else */
+#define EP_STATUS_WORDS 16
 
 /* ---- problem flags ---------------------------------------------------- */
 #define EP_FLAG_ZERO_PADDING 1 /* dispatch zeroes the alignment padding rows */
@@ -145,7 +158,20 @@ typedef struct ep_problem {
  *   row_topk_weights[row_capacity*K]      fp32: topk_weights[t,k] under the
  *                      same condition, else 0
  *   row_capacity       rows the three lists hold; if R exceeds it the lists
- *                      are not written and EP_STATUS_LIST_OVERFLOW is set. */
+ *                      are not written and EP_STATUS_LIST_OVERFLOW is set.
+ * Stale-layout guard (host field, not a device pointer):
+ *   generation         set by every ep_layout to a value unique in the
+ *                      process (never 0), which it also stamps into the
+ *                      device word EP_STATUS_GENERATION in stream order.  A
+ *                      copy of this struct taken after ep_layout is a cached
+ *                      handle to that layout: ep_dispatch, ep_combine and
+ *                      ep_expert_gemm compare the copy's generation with the
+ *                      device word and, if a later ep_layout has rewritten
+ *                      the buffers, write nothing and set EP_STATUS_STALE
+ *                      (the PR's cached handle= dispatch, rejected once the
+ *                      buffer's _layout_generation has moved on; commit
+ *                      adding the cached-layout dispatch).  A zeroed struct
+ *                      that no ep_layout has stamped fails the check. */
 typedef struct ep_layout {
   int32_t* counts;
   int32_t* offsets;
@@ -161,16 +187,21 @@ typedef struct ep_layout {
   int32_t* expert_row_src;
   int64_t expert_row_capacity;
   uint32_t* recv_stats;
+  uint32_t generation;
 } ep_layout_t;
 
 /* Bytes of one packed fp8 row: H bytes of E4M3FN payload, then H/128
  * little-endian fp32 scales, zero-padded to a multiple of 16 bytes
  * (hidden 7168 -> 7392, hidden 128 -> 144).  Returns -1 if hidden <= 0 or
- * hidden % 128 != 0.  Host only; no device work. */
+ * hidden % 128 != 0.  Host only; no device work.
+ * Defined by: TileScale PR #68, commit packing the fp8 payload and its
+ * scales into one row (row = payload, then scales, 16-byte padded). */
 int64_t ep_fp8_row_bytes(int32_t hidden);
 
 /* Bytes of device workspace ep_layout needs for this problem (per-block
- * partial counts).  Returns 0 for an invalid problem.  Host only. */
+ * partial counts).  Returns 0 for an invalid problem.  Host only.
+ * Defined by: TileScale PR #68, Design section (per-block counts that a
+ * prefix sum turns into bases). */
 size_t ep_layout_workspace_bytes(const ep_problem_t* p);
 
 /* Layout: phase 1 (count per expert, and per group), phase 2 (exclusive
@@ -178,12 +209,18 @@ size_t ep_layout_workspace_bytes(const ep_problem_t* p);
  * [T*K] row-major.  topk_weights fp32 [T*K] is read only to fill
  * row_topk_weights and may be NULL when num_groups == 0.  `workspace` must
  * hold ep_layout_workspace_bytes(p) bytes (contents need no initialisation
- * and are clobbered).  Writes every output of `L` listed above, including
- * all status words except EP_STATUS_COMBINE_OOB, which it clears.
- * Placement is deterministic: identical inputs give identical bytes. */
+ * and are clobbered).  Writes every output of `L` listed above and every
+ * status word (EP_STATUS_COMBINE_OOB, _DISPATCH_OVERFLOW and _STALE as 0),
+ * and sets L->generation (host field) to a fresh value that it also stamps
+ * into EP_STATUS_GENERATION.  Placement is deterministic: identical inputs
+ * give identical bytes.
+ * Defined by: TileScale PR #68, Design section (count, exclusive prefix
+ * sum, slot claimed under the base); commit adding DeepEP's do_expand (the
+ * destination is the expert, segments expert-major, expert_alignment,
+ * -1 entries skipped); commit on masked topk_idx; commit adding the
+ * expanded combine (per-row local expert ids and weights, recv_topk_idx). */
 int ep_layout(const ep_problem_t* p, const int64_t* topk_idx, const float* topk_weights,
-              const ep_layout_t* L, void* workspace, size_t workspace_bytes,
-              hipStream_t stream);
+              ep_layout_t* L, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Dispatch: scatter every token row of x (bf16 [T*H]) to the receive rows
  * the layout assigned it (with EP_FLAG_ZERO_PADDING also zero the expert
@@ -205,11 +242,19 @@ int ep_layout(const ep_problem_t* p, const int64_t* topk_idx, const float* topk_
  * the next row are never written.  recv must hold capacity_rows rows.
  * Each source row is read once and written once per destination row.  If
  * the rows needed (status word EP_STATUS_ROWS_EXPERT or _GROUP) exceed
- * capacity_rows the call writes nothing: an overflow is known before any
- * payload moves.  Rows at or beyond the rows needed are never touched.
+ * capacity_rows the call writes no row and sets EP_STATUS_DISPATCH_OVERFLOW
+ * to 1 (else it sets it to 0): an overflow is known before any payload
+ * moves.  Rows at or beyond the rows needed are never touched.  If L's
+ * generation is not the one stamped on its buffers, the call writes nothing
+ * but EP_STATUS_STALE = 1.
  * Base pointers of x and recv, and the stride, must be 16-byte aligned for
  * the fp8 format; for bf16 any 2-byte alignment works (wider alignment is
- * faster). */
+ * faster).
+ * Defined by: TileScale PR #68, summary and Design section (each row
+ * written once, at its final compact index); commit adding DeepEP's
+ * do_expand (expert-major rows, expand_overflow, zero_padding); commit
+ * packing the fp8 payload and scales into one row; PR description,
+ * Testing section (per-token, per-128 fp8 cast). */
 int ep_dispatch(const ep_problem_t* p, const ep_layout_t* L, const void* x, void* recv,
                 int64_t capacity_rows, int64_t recv_row_stride, int32_t rows, int32_t format,
                 hipStream_t stream);
@@ -230,7 +275,13 @@ int ep_dispatch(const ep_problem_t* p, const ep_layout_t* L, const void* x, void
  * commit adding receive stats and combine bias).  In the grouped order the
  * bias seeds the cross-group total.  A slot >= y_rows is skipped and sets
  * status word EP_STATUS_COMBINE_OOB.  Every one of the T output rows is
- * written. */
+ * written, unless L's generation is not the one stamped on its buffers:
+ * then the call writes nothing but EP_STATUS_STALE = 1.
+ * Defined by: TileScale PR #68, summary and Design section (one reduce per
+ * source token over its gathered rows); commit on masked topk_idx (-1
+ * skipped, a fully masked token gives zero); commit adding the expanded
+ * combine, kDoExpandedSend (sum within the group first); commit adding
+ * receive stats and combine bias. */
 int ep_combine(const ep_problem_t* p, const ep_layout_t* L, const int64_t* topk_idx,
                const float* topk_weights, const void* y, int64_t y_rows, const void* bias0,
                const void* bias1, void* out, int32_t order, hipStream_t stream);
@@ -261,7 +312,10 @@ int ep_combine(const ep_problem_t* p, const ep_layout_t* L, const int64_t* topk_
  * Requires H % 64 == 0 and n_out % 128 == 0, and
  * at most 2^31 - 1 output tiles of 320 x 256 (EP_ENOTSUP otherwise), 16-byte
  * aligned x, w and y, x_row_stride a multiple of 8 and y_row_stride a
- * multiple of 4. */
+ * multiple of 4.  If L's generation is not the one stamped on its buffers,
+ * the call writes nothing but EP_STATUS_STALE = 1.
+ * Defined by: the mKernel article ("Introducing mKernel"), its table of
+ * fused kernels (MoE dispatch + grouped GEMM). */
 int ep_expert_gemm(const ep_problem_t* p, const ep_layout_t* L, const void* x,
                    int64_t x_row_stride, const void* w, int32_t n_out, void* y,
                    int64_t y_row_stride, hipStream_t stream);
@@ -285,7 +339,7 @@ int64_t ep_expert_weights_packed_bytes(int32_t num_experts, int32_t n_out, int32
 int ep_pack_expert_weights(const void* w, int32_t num_experts, int32_t n_out, int32_t hidden,
                            void* w_packed, hipStream_t stream);
 
-/* Static description of a return code. */
+/* Static description of a return code.  Not from the pages. */
 const char* ep_strerror(int code);
 
 #ifdef __cplusplus

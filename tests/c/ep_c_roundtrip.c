@@ -25,6 +25,11 @@
  * both must equal the bf16 rounding (nearest, ties to even) of the exact
  * sum, computed here on the host.
  *
+ * A dispatch one row short of capacity must write nothing and set the
+ * overflow status word; a copy of the layout struct taken before a later
+ * ep_layout on the same buffers (a stale cached handle) must make dispatch
+ * and combine write nothing and set the stale word.
+ *
  * Prints "OK" and exits 0 on success; prints the first mismatch and exits
  * 1 otherwise.
  */
@@ -266,6 +271,96 @@ int main(void) {
     hipFree(d_recv8);
   }
 
+  /* Dispatch overflow and the stale-layout guard.  A capacity one row short
+     writes no row and raises EP_STATUS_DISPATCH_OVERFLOW; a copy of the
+     layout struct taken before a later ep_layout on the same buffers is a
+     stale handle: dispatch and combine then write nothing and raise the
+     sticky EP_STATUS_STALE, which the next ep_layout clears. */
+  {
+    const size_t nbytes = (size_t)T * K * H * 2;
+    static uint8_t poison[(size_t)T * K * H * 2];
+    uint8_t* d_poison;
+    uint16_t* d_out2;
+    size_t i;
+    CHECK_HIP(hipMalloc((void**)&d_poison, nbytes));
+    CHECK_HIP(hipMalloc((void**)&d_out2, sizeof out));
+    CHECK_HIP(hipMemset(d_poison, 0xAB, nbytes));
+    CHECK_HIP(hipMemset(d_out2, 0xCD, sizeof out));
+    CHECK_EP(ep_dispatch(&p, &L, d_x, d_poison, n_sel - 1, 0, EP_ROWS_EXPERT, EP_FORMAT_BF16, s));
+    CHECK_HIP(hipStreamSynchronize(s));
+    CHECK_HIP(hipMemcpy(status, d_status, sizeof status, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(poison, d_poison, nbytes, hipMemcpyDeviceToHost));
+    if (status[EP_STATUS_DISPATCH_OVERFLOW] != 1 || status[EP_STATUS_STALE] != 0) {
+      printf("capacity n_sel - 1: overflow word %d, stale word %d, expected 1, 0\n",
+             status[EP_STATUS_DISPATCH_OVERFLOW], status[EP_STATUS_STALE]);
+      return 1;
+    }
+    for (i = 0; i < nbytes; ++i)
+      if (poison[i] != 0xAB) {
+        printf("overflowing dispatch wrote byte %zu\n", i);
+        return 1;
+      }
+    CHECK_EP(ep_dispatch(&p, &L, d_x, d_poison, n_sel, 0, EP_ROWS_EXPERT, EP_FORMAT_BF16, s));
+    CHECK_HIP(hipStreamSynchronize(s));
+    CHECK_HIP(hipMemcpy(status, d_status, sizeof status, hipMemcpyDeviceToHost));
+    if (status[EP_STATUS_DISPATCH_OVERFLOW] != 0) {
+      printf("capacity n_sel: overflow word %d, expected 0\n", status[EP_STATUS_DISPATCH_OVERFLOW]);
+      return 1;
+    }
+
+    const ep_layout_t old = L; /* a cached handle to this layout */
+    if (L.generation == 0 || (uint32_t)status[EP_STATUS_GENERATION] != L.generation) {
+      printf("generation %u, device stamp %d\n", L.generation, status[EP_STATUS_GENERATION]);
+      return 1;
+    }
+    CHECK_EP(ep_layout(&p, d_idx, d_w, &L, d_ws, ws_bytes, s)); /* same buffers rewritten */
+    if (L.generation == old.generation) {
+      printf("ep_layout did not advance the generation\n");
+      return 1;
+    }
+    CHECK_HIP(hipMemset(d_poison, 0xAB, nbytes));
+    CHECK_EP(ep_dispatch(&p, &old, d_x, d_poison, T * K, 0, EP_ROWS_EXPERT, EP_FORMAT_BF16, s));
+    CHECK_EP(ep_combine(&p, &old, NULL, d_w, d_recv, T * K, NULL, NULL, d_out2, EP_COMBINE_FLAT, s));
+    CHECK_HIP(hipStreamSynchronize(s));
+    CHECK_HIP(hipMemcpy(status, d_status, sizeof status, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(poison, d_poison, nbytes, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(out, d_out2, sizeof out, hipMemcpyDeviceToHost));
+    if (status[EP_STATUS_STALE] != 1) {
+      printf("stale handle: stale word %d, expected 1\n", status[EP_STATUS_STALE]);
+      return 1;
+    }
+    for (i = 0; i < nbytes; ++i)
+      if (poison[i] != 0xAB) {
+        printf("dispatch with a stale handle wrote byte %zu\n", i);
+        return 1;
+      }
+    for (i = 0; i < (size_t)T * H; ++i)
+      if (out[i] != 0xCDCD) {
+        printf("combine with a stale handle wrote element %zu\n", i);
+        return 1;
+      }
+    /* the current handle works, and the next layout clears the flag */
+    CHECK_EP(ep_combine(&p, &L, NULL, d_w, d_recv, T * K, NULL, NULL, d_out2, EP_COMBINE_FLAT, s));
+    CHECK_HIP(hipStreamSynchronize(s));
+    CHECK_HIP(hipMemcpy(out, d_out2, sizeof out, hipMemcpyDeviceToHost));
+    for (t = 0; t < T; ++t)
+      for (h = 0; h < H; ++h)
+        if (int_of_bf16(out[t * H + h]) != keff[t] * ((t * 13 + h * 7) % 15 - 7)) {
+          printf("combine with the current handle: token %d element %d wrong\n", t, h);
+          return 1;
+        }
+    CHECK_EP(ep_layout(&p, d_idx, d_w, &L, d_ws, ws_bytes, s));
+    CHECK_HIP(hipStreamSynchronize(s));
+    CHECK_HIP(hipMemcpy(status, d_status, sizeof status, hipMemcpyDeviceToHost));
+    if (status[EP_STATUS_STALE] != 0 || (uint32_t)status[EP_STATUS_GENERATION] != L.generation) {
+      printf("after a new layout: stale word %d, stamp %d (generation %u)\n", status[EP_STATUS_STALE],
+             status[EP_STATUS_GENERATION], L.generation);
+      return 1;
+    }
+    hipFree(d_poison);
+    hipFree(d_out2);
+  }
+
   /* grouped rows and the grouped combine order */
   {
     enum { G = 4, EPG = E / G };
@@ -400,6 +495,9 @@ int main(void) {
     CHECK_HIP(hipMalloc((void**)&d_y, sizeof y));
     CHECK_HIP(hipMalloc((void**)&d_yp, sizeof yp));
     CHECK_HIP(hipMemcpy(d_wg, wg, sizeof wg, hipMemcpyHostToDevice));
+    /* the grouped layout above rewrote these buffers (it shares them), so
+       the flat layout is computed again for a current handle */
+    CHECK_EP(ep_layout(&p, d_idx, d_w, &L, d_ws, ws_bytes, s));
     CHECK_EP(ep_expert_gemm(&p, &L, d_recv, 0, d_wg, N, d_y, 0, s));
     CHECK_EP(ep_pack_expert_weights(d_wg, E, N, H, d_wp, s));
     {
@@ -440,7 +538,8 @@ int main(void) {
   hipFree(d_ws);
   hipStreamDestroy(s);
   printf("OK: %d selections, %d invalid ids, combine of the dispatched rows = K_eff * x, "
-         "fp8 rows exact, grouped rows, lists and grouped combine exact, "
+         "fp8 rows exact, overflow and stale handles write nothing and are flagged, "
+         "grouped rows, lists and grouped combine exact, "
          "grouped GEMM exact (plain and packed weights)\n",
          n_sel, n_invalid);
   return 0;

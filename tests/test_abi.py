@@ -151,6 +151,7 @@ def test_expert_gemm_host_checks():
     lay = _lib.LayoutStruct()
     lay.counts = 256
     lay.offsets = 256
+    lay.status = 256
     fake = ctypes.c_void_p(1 << 20)
     p = _lib.Problem(1 << 20, 7168, 8, 1024, 0, 0, 0)
     # hidden % 64 and n_out % 128

@@ -136,8 +136,11 @@ def test_layout_repeat_bit_identical():
     n = L0.num_rows(ep().EP_ROWS_GROUP)
 
     def outs(L):
-        # row lists hold n rows; the rest of their capacity is never written
-        return (L.slot, L.grow, L.row_src[:n], L.row_topk_idx[:n], L.row_topk_weights[:n], L.status)
+        # row lists hold n rows; the rest of their capacity is never written.
+        # Every status word but the generation stamp (a new one per call).
+        st = L.status.clone()
+        st[ep().EP_STATUS_GENERATION] = 0
+        return (L.slot, L.grow, L.row_src[:n], L.row_topk_idx[:n], L.row_topk_weights[:n], st)
 
     ref = [t.clone() for t in outs(L0)]
     for _ in range(200):

@@ -44,6 +44,8 @@ __all__ = [
     "fp8_row_pitch",
     "ep_layout_workspace_bytes",
     "ep_layout",
+    "ep_layout_noalloc",
+    "alloc_layout",
     "ep_dispatch",
     "ep_combine",
     "ep_expert_gemm",
@@ -215,52 +217,24 @@ def _resolve(layout) -> tuple[Layout, int]:
     return layout, layout.generation
 
 
-def ep_layout(
-    topk_idx: torch.Tensor,
-    num_experts: int,
-    num_groups: int = 0,
-    topk_weights: torch.Tensor | None = None,
-    row_capacity: int | None = None,
-    out: Layout | None = None,
-    expert_alignment: int = 0,
-    expert_row_src: bool = False,
-    recv_stats: torch.Tensor | None = None,
-) -> Layout:
-    """Count, scan and place every selection of topk_idx (int64 [T, K]).
-
-    ``expert_alignment`` rounds each expert segment up to a multiple of that
-    many rows; ``expert_row_src`` also returns each expert-major row's source
-    token (-1 on padding rows); ``recv_stats`` (uint32 as int32 [E]) gets the
-    per-expert counts added to it.  ``out`` reuses the buffers of an earlier
-    Layout of the same shape (nothing is allocated then; its generation
-    advances)."""
+def _check_layout_args(topk_idx, num_experts, num_groups, topk_weights, recv_stats):
     if topk_idx.dim() != 2:
         raise ValueError("topk_idx must be [T, K]")
     T, K = topk_idx.shape
     _dev(topk_idx, "topk_idx", torch.int64)
-    dev = topk_idx.device
-    G = int(num_groups)
-    A = int(expert_alignment)
     if topk_weights is not None:
         _dev(topk_weights, "topk_weights", torch.float32, (T, K))
+    elif int(num_groups) > 0:
+        raise ValueError("grouped layout needs topk_weights for the per-row weight lists")
     if recv_stats is not None:
         if recv_stats.dtype not in (torch.int32, torch.uint32):
             raise TypeError("recv_stats must be a 32-bit integer tensor")
         _dev(recv_stats, "recv_stats", recv_stats.dtype, (num_experts,))
-    if out is not None:
-        if (out.num_tokens, out.topk, out.num_experts, out.num_groups, out.expert_alignment) != (
-            T,
-            K,
-            num_experts,
-            G,
-            A,
-        ):
-            raise ValueError("out was allocated for a different problem shape")
-        if G > 0 and topk_weights is None:
-            raise ValueError("grouped layout needs topk_weights for the per-row weight lists")
-        out.recv_stats = recv_stats
-        _run_layout(out, topk_idx, topk_weights)
-        return out
+    return T, K
+
+
+def _alloc_layout(T, K, num_experts, G, A, dev, row_capacity, expert_row_src, recv_stats) -> Layout:
+    """A Layout's output buffers for this shape (no workspace)."""
     i32 = dict(dtype=torch.int32, device=dev)
     L = Layout(
         num_tokens=T,
@@ -286,13 +260,53 @@ def ep_layout(
         L.row_src = torch.empty(max(cap, 1), **i32)
         L.row_topk_idx = torch.empty(max(cap, 1), K, **i32)
         L.row_topk_weights = torch.empty(max(cap, 1), K, dtype=torch.float32, device=dev)
-        if topk_weights is None:
-            raise ValueError("grouped layout needs topk_weights for the per-row weight lists")
+    return L
+
+
+def _check_out_shape(out: Layout, T, K, num_experts, G, A) -> None:
+    if (out.num_tokens, out.topk, out.num_experts, out.num_groups, out.expert_alignment) != (
+        T,
+        K,
+        num_experts,
+        G,
+        A,
+    ):
+        raise ValueError("out was allocated for a different problem shape")
+
+
+def ep_layout(
+    topk_idx: torch.Tensor,
+    num_experts: int,
+    num_groups: int = 0,
+    topk_weights: torch.Tensor | None = None,
+    row_capacity: int | None = None,
+    out: Layout | None = None,
+    expert_alignment: int = 0,
+    expert_row_src: bool = False,
+    recv_stats: torch.Tensor | None = None,
+) -> Layout:
+    """Count, scan and place every selection of topk_idx (int64 [T, K]).
+
+    ``expert_alignment`` rounds each expert segment up to a multiple of that
+    many rows; ``expert_row_src`` also returns each expert-major row's source
+    token (-1 on padding rows); ``recv_stats`` (uint32 as int32 [E]) gets the
+    per-expert counts added to it.  ``out`` reuses the buffers of an earlier
+    Layout of the same shape (nothing is allocated then; its generation
+    advances)."""
+    T, K = _check_layout_args(topk_idx, num_experts, num_groups, topk_weights, recv_stats)
+    G = int(num_groups)
+    A = int(expert_alignment)
+    if out is not None:
+        _check_out_shape(out, T, K, num_experts, G, A)
+        out.recv_stats = recv_stats
+        _run_layout(out, topk_idx, topk_weights)
+        return out
+    L = _alloc_layout(T, K, num_experts, G, A, topk_idx.device, row_capacity, expert_row_src, recv_stats)
     p = _problem(T, 1, K, num_experts, G, A)
     nbytes = int(_lib.lib().ep_layout_workspace_bytes(ctypes.byref(p)))
     if nbytes == 0:
         raise _lib.EPError("ep_layout_workspace_bytes", _lib.EP_EINVAL, "invalid problem shape")
-    L.workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    L.workspace = torch.empty(nbytes, dtype=torch.uint8, device=topk_idx.device)
     _run_layout(L, topk_idx, topk_weights)
     return L
 
@@ -300,6 +314,9 @@ def ep_layout(
 def _run_layout(L: Layout, topk_idx: torch.Tensor, topk_weights: torch.Tensor | None) -> None:
     p = _problem(L.num_tokens, 1, L.topk, L.num_experts, L.num_groups, L.expert_alignment)
     s = L.struct()
+    if L.workspace is None:
+        raise ValueError("this Layout has no workspace (made by ep_layout_noalloc); pass it to "
+                         "ep_layout_noalloc, or make one with ep_layout")
     rc = _lib.lib().ep_layout(
         ctypes.byref(p),
         _ptr(topk_idx),
@@ -311,6 +328,49 @@ def _run_layout(L: Layout, topk_idx: torch.Tensor, topk_weights: torch.Tensor | 
     )
     _lib.check("ep_layout", rc)
     L.generation = int(s.generation)
+
+
+def ep_layout_noalloc(
+    topk_idx: torch.Tensor,
+    num_experts: int,
+    out: Layout,
+    topk_weights: torch.Tensor | None = None,
+    recv_stats: torch.Tensor | None = None,
+) -> Layout:
+    """ep_layout into the buffers of ``out`` (a Layout of the same shape, from
+    ep_layout or ``alloc_layout``) with no device allocation at all: the
+    library keeps the per-block tallies in its own fixed per-GPU scratch
+    (EP_LAYOUT_SCRATCH_BYTES), so this call suits code that must not
+    allocate (graph capture, serving loops).  Calls on one GPU share that
+    scratch and must not overlap in time.  Raises EPError (EP_ESCRATCH) for
+    a problem whose tallies do not fit it."""
+    T, K = _check_layout_args(topk_idx, num_experts, out.num_groups, topk_weights, recv_stats)
+    _check_out_shape(out, T, K, num_experts, out.num_groups, out.expert_alignment)
+    out.recv_stats = recv_stats
+    p = _problem(T, 1, K, num_experts, out.num_groups, out.expert_alignment)
+    s = out.struct()
+    rc = _lib.lib().ep_layout_noalloc(
+        ctypes.byref(p), _ptr(topk_idx), _ptr(topk_weights), ctypes.byref(s), _stream(topk_idx.device)
+    )
+    _lib.check("ep_layout_noalloc", rc)
+    out.generation = int(s.generation)
+    return out
+
+
+def alloc_layout(
+    num_tokens: int,
+    topk: int,
+    num_experts: int,
+    num_groups: int = 0,
+    row_capacity: int | None = None,
+    expert_alignment: int = 0,
+    expert_row_src: bool = False,
+    device: torch.device | str = "cuda",
+) -> Layout:
+    """The output buffers of a layout of this shape, without a workspace, for
+    ``ep_layout_noalloc`` (allocate once, outside the code that must not)."""
+    return _alloc_layout(int(num_tokens), int(topk), int(num_experts), int(num_groups),
+                         int(expert_alignment), torch.device(device), row_capacity, expert_row_src, None)
 
 
 def ep_dispatch(

@@ -17,9 +17,11 @@ EP_EINVAL = 1
 EP_ENOTSUP = 2
 EP_EHIP = 3
 EP_EWORKSPACE = 4
+EP_ESCRATCH = 5
 
 EP_MAX_TOPK = 32
 EP_MAX_KEYS = 1024
+EP_LAYOUT_SCRATCH_BYTES = 4 << 20
 
 EP_STATUS_INVALID_IDS = 0
 EP_STATUS_ROWS_EXPERT = 1
@@ -48,6 +50,7 @@ EXPORTS = (
     "ep_fp8_row_bytes",
     "ep_layout_workspace_bytes",
     "ep_layout",
+    "ep_layout_noalloc",
     "ep_dispatch",
     "ep_combine",
     "ep_expert_gemm",
@@ -118,6 +121,8 @@ def lib(path: str | None = None) -> ctypes.CDLL:
     L.ep_layout_workspace_bytes.restype = ctypes.c_size_t
     L.ep_layout.argtypes = [P, vp, vp, LS, vp, ctypes.c_size_t, vp]
     L.ep_layout.restype = ctypes.c_int
+    L.ep_layout_noalloc.argtypes = [P, vp, vp, LS, vp]
+    L.ep_layout_noalloc.restype = ctypes.c_int
     L.ep_dispatch.argtypes = [P, LS, vp, vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, vp]
     L.ep_dispatch.restype = ctypes.c_int
     L.ep_combine.argtypes = [P, LS, vp, vp, vp, ctypes.c_int64, vp, vp, vp, ctypes.c_int32, vp]

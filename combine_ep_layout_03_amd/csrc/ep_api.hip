@@ -4,9 +4,16 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "ep_internal.h"
 #include "ep_mi355x.h"
+
+// Layout scratch of ep_layout_noalloc: one array per GPU, in the code
+// object, zero at load and held until the process ends.  Host code never
+// passes `scratch` itself to a kernel (on the host it only names the
+// symbol); it passes the device address scratch_on_current_device() looks up.
+static __device__ __align__(256) unsigned char scratch[EP_LAYOUT_SCRATCH_BYTES];
 
 namespace {
 
@@ -24,6 +31,24 @@ uint32_t next_generation() {
     g = counter.fetch_add(1, std::memory_order_relaxed) + 1;
   } while (g == 0);
   return g;
+}
+
+constexpr int kMaxDevices = 64;
+
+// The current device's address of `scratch`, looked up once per device
+// (with that device current) and kept; null if the lookup fails.
+void* scratch_on_current_device() {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    addr[dev] = ptr;
+  }
+  return addr[dev];
 }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -119,6 +144,17 @@ int ep_layout(const ep_problem_t* p, const int64_t* topk_idx, const float* topk_
   if (ep::launch_layout(a, g, stream) != hipSuccess) return EP_EHIP;
   L->generation = a.generation;
   return EP_OK;
+}
+
+int ep_layout_noalloc(const ep_problem_t* p, const int64_t* topk_idx, const float* topk_weights,
+                      ep_layout_t* L, hipStream_t stream) {
+  const int rc = check_problem(p);
+  if (rc != EP_OK) return rc;
+  const ep::LayoutGeom g = ep::layout_geom(p->num_tokens * p->topk, p->num_experts, p->num_groups);
+  if (ep::layout_workspace_bytes(g) > EP_LAYOUT_SCRATCH_BYTES) return EP_ESCRATCH;
+  void* ws = scratch_on_current_device();
+  if (!ws) return EP_EHIP;
+  return ep_layout(p, topk_idx, topk_weights, L, ws, EP_LAYOUT_SCRATCH_BYTES, stream);
 }
 
 int ep_dispatch(const ep_problem_t* p, const ep_layout_t* L, const void* x, void* recv,
@@ -286,6 +322,8 @@ const char* ep_strerror(int code) {
       return "unsupported (fp8 needs hidden % 128 == 0 and hidden <= 32768; K <= 32; E + G <= 1024)";
     case EP_EHIP: return "HIP launch failed";
     case EP_EWORKSPACE: return "workspace smaller than ep_layout_workspace_bytes()";
+    case EP_ESCRATCH:
+      return "problem needs more layout scratch than EP_LAYOUT_SCRATCH_BYTES (use ep_layout with a workspace)";
     default: return "unknown error code";
   }
 }

@@ -53,10 +53,13 @@ extern "C" {
 #define EP_ENOTSUP 2    /* valid but unsupported (fp8 with hidden % 128 != 0, limits) */
 #define EP_EHIP 3       /* a HIP launch failed (hipGetLastError) */
 #define EP_EWORKSPACE 4 /* workspace smaller than ep_layout_workspace_bytes() */
+#define EP_ESCRATCH 5   /* ep_layout_noalloc: the problem needs more than the
+                         * library's fixed EP_LAYOUT_SCRATCH_BYTES of scratch */
 
 /* ---- limits ---------------------------------------------------------- */
 #define EP_MAX_TOPK 32     /* K */
 #define EP_MAX_KEYS 1024   /* E + G (destinations counted by the layout) */
+#define EP_LAYOUT_SCRATCH_BYTES (4u << 20) /* ep_layout_noalloc's fixed scratch, per GPU */
 
 /* ---- device status words ---------------------------------------------
  * ep_layout writes every word (words 4, 7 and 9 as 0); the other calls
@@ -221,6 +224,24 @@ size_t ep_layout_workspace_bytes(const ep_problem_t* p);
  * expanded combine (per-row local expert ids and weights, recv_topk_idx). */
 int ep_layout(const ep_problem_t* p, const int64_t* topk_idx, const float* topk_weights,
               ep_layout_t* L, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ep_layout without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Identical outputs to ep_layout; the
+ * per-block tallies live instead in a library-owned device array of
+ * EP_LAYOUT_SCRATCH_BYTES, one per GPU, held until the process ends.  The
+ * call allocates and frees nothing.  Returns EP_ESCRATCH, with nothing
+ * enqueued, if ep_layout_workspace_bytes(p) exceeds EP_LAYOUT_SCRATCH_BYTES
+ * (that size is 4 * (layout blocks + 1) * (E + G + 1) bytes rounded up to
+ * 256, with at most 2048 layout blocks, so every problem with E + G <= 510
+ * fits, at any T); EP_EHIP if the array's device
+ * address cannot be found on the current device.  Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (two
+ * streams, or two host threads) race and must be ordered by the caller.
+ * Nothing in the array needs to start at zero (the tallies are written
+ * before they are read). */
+int ep_layout_noalloc(const ep_problem_t* p, const int64_t* topk_idx, const float* topk_weights,
+                      ep_layout_t* L, hipStream_t stream);
 
 /* Dispatch: scatter every token row of x (bf16 [T*H]) to the receive rows
  * the layout assigned it (with EP_FLAG_ZERO_PADDING also zero the expert

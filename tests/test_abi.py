@@ -22,6 +22,7 @@ def test_header_declares_the_boundary():
             "ep_fp8_row_bytes",
             "ep_layout_workspace_bytes",
             "ep_layout",
+            "ep_layout_noalloc",
             "ep_dispatch",
             "ep_combine",
             "ep_expert_gemm",
@@ -49,7 +50,8 @@ int use(void) {
   ep_problem_t p = {0};
   ep_layout_t l = {0};
   (void)ep_fp8_row_bytes(128); (void)ep_layout_workspace_bytes(&p);
-  (void)ep_layout(&p, 0, 0, &l, 0, 0, 0); (void)ep_dispatch(&p, &l, 0, 0, 0, 0, 0, 0, 0);
+  (void)ep_layout(&p, 0, 0, &l, 0, 0, 0); (void)ep_layout_noalloc(&p, 0, 0, &l, 0);
+  (void)ep_dispatch(&p, &l, 0, 0, 0, 0, 0, 0, 0);
   (void)ep_combine(&p, &l, 0, 0, 0, 0, 0, 0, 0, 0, 0);
   (void)ep_expert_gemm(&p, &l, 0, 0, 0, 0, 0, 0, 0); (void)ep_strerror(0);
   return 0;
@@ -96,7 +98,7 @@ def test_host_only_entry_points():
     assert ep.ep_expert_weights_packed_bytes(3, 100, 128) == -1  # N % 128
     assert ep.ep_expert_weights_packed_bytes(3, 256, 96) == -1  # H % 64
     assert ep.ep_expert_weights_packed_bytes(0, 256, 128) == -1
-    for c in range(5):
+    for c in range(6):
         assert ep.ep_strerror(c)
 
 
@@ -139,6 +141,29 @@ def test_invalid_arguments_return_codes_before_any_launch():
     p4 = _lib.Problem(16, 32768 + 128, 8, 256, 0, 0, 0)
     assert L.ep_dispatch(ctypes.byref(p4), ctypes.byref(lay), None, None, 0, 0, 0, 1, None) == _lib.EP_ENOTSUP
     assert L.ep_combine(ctypes.byref(p0), ctypes.byref(lay), None, None, None, 0, None, None, None, 0, None) == _lib.EP_OK
+
+
+def test_noalloc_layout_refuses_oversized_problems_on_the_host():
+    """ep_layout_noalloc checks the problem's tallies against its fixed
+    scratch before any pointer is used or any device call made: too large a
+    problem returns EP_ESCRATCH (null pointers here are never dereferenced),
+    and a bad shape EP_EINVAL / EP_ENOTSUP as ep_layout would."""
+    from combine_ep_layout_03_amd import _lib
+
+    L = _lib.lib()
+    lay = _lib.LayoutStruct()
+    big = _lib.Problem(37500, 1, 8, 1000, 0, 0, 0)
+    assert L.ep_layout_workspace_bytes(ctypes.byref(big)) > _lib.EP_LAYOUT_SCRATCH_BYTES
+    assert L.ep_layout_noalloc(ctypes.byref(big), None, None, ctypes.byref(lay), None) == _lib.EP_ESCRATCH
+    # the largest grid at E + G = 510 still fits, at 511 it does not
+    fits = _lib.Problem(1 << 20, 1, 8, 510, 0, 0, 0)
+    over = _lib.Problem(1 << 20, 1, 8, 511, 0, 0, 0)
+    assert L.ep_layout_workspace_bytes(ctypes.byref(fits)) <= _lib.EP_LAYOUT_SCRATCH_BYTES
+    assert L.ep_layout_noalloc(ctypes.byref(over), None, None, ctypes.byref(lay), None) == _lib.EP_ESCRATCH
+    assert L.ep_layout_noalloc(ctypes.byref(_lib.Problem(16, 1, 0, 256, 0, 0, 0)), None, None, ctypes.byref(lay),
+                               None) == _lib.EP_EINVAL
+    assert L.ep_layout_noalloc(ctypes.byref(_lib.Problem(16, 1, 33, 256, 0, 0, 0)), None, None, ctypes.byref(lay),
+                               None) == _lib.EP_ENOTSUP
 
 
 def test_expert_gemm_host_checks():

@@ -21,7 +21,7 @@ EP_ESCRATCH = 5
 
 EP_MAX_TOPK = 32
 EP_MAX_KEYS = 1024
-EP_LAYOUT_SCRATCH_BYTES = 4 << 20
+EP_LAYOUT_SCRATCH_BYTES = 9 << 18
 
 EP_STATUS_INVALID_IDS = 0
 EP_STATUS_ROWS_EXPERT = 1

@@ -111,7 +111,7 @@ int ep_layout(const ep_problem_t* p, const int64_t* topk_idx, const float* topk_
       return EP_EINVAL;
   }
   if (L->expert_row_src && L->expert_row_capacity < 0) return EP_EINVAL;
-  if (!aligned(topk_idx, 8) || !aligned(workspace, 4)) return EP_EINVAL;
+  if (!aligned(topk_idx, 8) || !aligned(workspace, 16)) return EP_EINVAL;
 
   const ep::LayoutGeom g = ep::layout_geom(T * p->topk, p->num_experts, p->num_groups);
   if (workspace_bytes < ep::layout_workspace_bytes(g)) return EP_EWORKSPACE;

@@ -7,12 +7,18 @@
 
 namespace ep {
 
-// Geometry of the layout kernels: block b counts entries
-// [b * rounds * 256, (b + 1) * rounds * 256) of the flattened (t,k) order.
+// Geometry of the layout kernels.  Place block b handles entries
+// [b * rounds * 256, (b + 1) * rounds * 256) of the flattened (t,k) order;
+// count block c tallies the `chunk` consecutive place blocks
+// [c * chunk, (c + 1) * chunk).
 struct LayoutGeom {
-  int nblocks;  // >= 1
-  int rounds;   // entries per thread
-  int ncols;    // E + G + 1 partial-count columns (last column: invalid ids)
+  int nblocks;  // place blocks, >= 1
+  int rounds;   // entries per place-block thread (a power of two)
+  int span_shift;  // log2 of a place block's entries, 8 + log2(rounds)
+  int half;     // count-block tallies in 16-bit halves (span <= 32768)
+  int ncols;    // E + G + 1 tally columns (last column: invalid ids)
+  int chunk;    // place blocks per count block, >= 1
+  int ncount;   // count blocks, ceil(nblocks / chunk)
 };
 
 LayoutGeom layout_geom(int64_t n_entries, int E, int G);

@@ -59,7 +59,7 @@ extern "C" {
 /* ---- limits ---------------------------------------------------------- */
 #define EP_MAX_TOPK 32     /* K */
 #define EP_MAX_KEYS 1024   /* E + G (destinations counted by the layout) */
-#define EP_LAYOUT_SCRATCH_BYTES (4u << 20) /* ep_layout_noalloc's fixed scratch, per GPU */
+#define EP_LAYOUT_SCRATCH_BYTES (9u << 18) /* ep_layout_noalloc's fixed scratch per GPU, 2.25 MiB */
 
 /* ---- device status words ---------------------------------------------
  * ep_layout writes every word (words 4, 7 and 9 as 0); the other calls
@@ -202,7 +202,8 @@ typedef struct ep_layout {
 int64_t ep_fp8_row_bytes(int32_t hidden);
 
 /* Bytes of device workspace ep_layout needs for this problem (per-block
- * partial counts).  Returns 0 for an invalid problem.  Host only.
+ * tallies and per-chunk totals; at most 2,230,528 bytes for any accepted
+ * problem).  Returns 0 for an invalid problem.  Host only.
  * Defined by: TileScale PR #68, Design section (per-block counts that a
  * prefix sum turns into bases). */
 size_t ep_layout_workspace_bytes(const ep_problem_t* p);
@@ -211,8 +212,8 @@ size_t ep_layout_workspace_bytes(const ep_problem_t* p);
  * scan into bases) and phase 3 (slots and grouped rows) for topk_idx int64
  * [T*K] row-major.  topk_weights fp32 [T*K] is read only to fill
  * row_topk_weights and may be NULL when num_groups == 0.  `workspace` must
- * hold ep_layout_workspace_bytes(p) bytes (contents need no initialisation
- * and are clobbered).  Writes every output of `L` listed above and every
+ * hold ep_layout_workspace_bytes(p) bytes, 16-byte aligned (contents need
+ * no initialisation and are clobbered).  Writes every output of `L` listed above and every
  * status word (EP_STATUS_COMBINE_OOB, _DISPATCH_OVERFLOW and _STALE as 0),
  * and sets L->generation (host field) to a fresh value that it also stamps
  * into EP_STATUS_GENERATION.  Placement is deterministic: identical inputs
@@ -230,11 +231,10 @@ int ep_layout(const ep_problem_t* p, const int64_t* topk_idx, const float* topk_
  * harnesses that forbid hipMalloc).  Identical outputs to ep_layout; the
  * per-block tallies live instead in a library-owned device array of
  * EP_LAYOUT_SCRATCH_BYTES, one per GPU, held until the process ends.  The
- * call allocates and frees nothing.  Returns EP_ESCRATCH, with nothing
- * enqueued, if ep_layout_workspace_bytes(p) exceeds EP_LAYOUT_SCRATCH_BYTES
- * (that size is 4 * (layout blocks + 1) * (E + G + 1) bytes rounded up to
- * 256, with at most 2048 layout blocks, so every problem with E + G <= 510
- * fits, at any T); EP_EHIP if the array's device
+ * call allocates and frees nothing.  The array covers every problem the
+ * library accepts (the largest ep_layout_workspace_bytes over all shapes is
+ * 2,230,528 bytes); EP_ESCRATCH, with nothing enqueued, guards a problem
+ * whose workspace would exceed it.  EP_EHIP if the array's device
  * address cannot be found on the current device.  Every call on one GPU
  * shares that GPU's array: calls that overlap in time on one GPU (two
  * streams, or two host threads) race and must be ordered by the caller.

@@ -143,23 +143,25 @@ def test_invalid_arguments_return_codes_before_any_launch():
     assert L.ep_combine(ctypes.byref(p0), ctypes.byref(lay), None, None, None, 0, None, None, None, 0, None) == _lib.EP_OK
 
 
-def test_noalloc_layout_refuses_oversized_problems_on_the_host():
-    """ep_layout_noalloc checks the problem's tallies against its fixed
-    scratch before any pointer is used or any device call made: too large a
-    problem returns EP_ESCRATCH (null pointers here are never dereferenced),
-    and a bad shape EP_EINVAL / EP_ENOTSUP as ep_layout would."""
+def test_noalloc_scratch_covers_every_layout_workspace():
+    """ep_layout_noalloc's fixed scratch holds the workspace of every problem
+    the library accepts: the workspace peaks where the place blocks reach
+    their cap at the widest tally rows (E + G = 1024, 131,072 entries:
+    2,230,528 bytes).  Shapes across the range are checked against the
+    scratch, and bad shapes still return EP_EINVAL / EP_ENOTSUP before any
+    device call (null pointers here are never dereferenced)."""
     from combine_ep_layout_03_amd import _lib
 
     L = _lib.lib()
     lay = _lib.LayoutStruct()
-    big = _lib.Problem(37500, 1, 8, 1000, 0, 0, 0)
-    assert L.ep_layout_workspace_bytes(ctypes.byref(big)) > _lib.EP_LAYOUT_SCRATCH_BYTES
-    assert L.ep_layout_noalloc(ctypes.byref(big), None, None, ctypes.byref(lay), None) == _lib.EP_ESCRATCH
-    # the largest grid at E + G = 510 still fits, at 511 it does not
-    fits = _lib.Problem(1 << 20, 1, 8, 510, 0, 0, 0)
-    over = _lib.Problem(1 << 20, 1, 8, 511, 0, 0, 0)
-    assert L.ep_layout_workspace_bytes(ctypes.byref(fits)) <= _lib.EP_LAYOUT_SCRATCH_BYTES
-    assert L.ep_layout_noalloc(ctypes.byref(over), None, None, ctypes.byref(lay), None) == _lib.EP_ESCRATCH
+    peak = 0
+    for keys in (1, 16, 256, 264, 511, 512, 1000, 1023, 1024):
+        for n in (1, 256, 65536, 131072, 262144, 500000, 524288, 1 << 22, 2147483640):
+            p = _lib.Problem(n // 8, 1, 8, keys, 0, 0, 0)
+            w = L.ep_layout_workspace_bytes(ctypes.byref(p))
+            assert 0 < w <= _lib.EP_LAYOUT_SCRATCH_BYTES, (keys, n, w)
+            peak = max(peak, w)
+    assert peak == 2230528
     assert L.ep_layout_noalloc(ctypes.byref(_lib.Problem(16, 1, 0, 256, 0, 0, 0)), None, None, ctypes.byref(lay),
                                None) == _lib.EP_EINVAL
     assert L.ep_layout_noalloc(ctypes.byref(_lib.Problem(16, 1, 33, 256, 0, 0, 0)), None, None, ctypes.byref(lay),

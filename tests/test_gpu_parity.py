@@ -447,41 +447,77 @@ def test_combine_fully_masked_and_oob():
 
 
 # --------------------------------------------------------------------------- grouped workload
-def test_grouped_workload_sampled():
-    """65536 tokens, 8 groups of 32 experts: layout in full, grouped dispatch
-    and grouped combine on sampled rows and tokens."""
+# 65,536 tokens, 8 groups of 32 experts, at its real size: the layout, every
+# one of the ~347 K grouped rows and every token's grouped combine against
+# the oracle, which runs over token chunks (slots renumbered per chunk) so
+# host memory stays bounded.
+CHUNK = 4096
+
+
+def _chunk_slots(dest_rows):
+    """A token chunk's destination rows renumbered over the rows it uses."""
+    used = np.unique(dest_rows[dest_rows >= 0])
+    remap = -np.ones(int(dest_rows.max(initial=-1)) + 2, np.int64)
+    remap[used] = np.arange(len(used))
+    return used, np.where(dest_rows >= 0, remap[np.maximum(dest_rows, 0)], -1)
+
+
+@pytest.fixture(scope="module")
+def grouped():
     w = W.by_name("grouped")
     say("grouped workload: inputs")
     idx, wt = W.make_routing(w)
     R = O.layout(idx.numpy(), w.E, w.G, wt.numpy())
-    x = W.make_x(w, device=DEV)
     d_idx, d_wt = idx.to(DEV), wt.to(DEV)
     L = ep().ep_layout(d_idx, w.E, w.G, d_wt)
-    check_layout(L, R, w.E, w.G)
+    return {"w": w, "idx": idx, "wt": wt, "R": R, "d_idx": d_idx, "d_wt": d_wt, "L": L}
+
+
+def test_grouped_workload_layout(grouped):
+    G = grouped
+    check_layout(G["L"], G["R"], G["w"].E, G["w"].G)
+
+
+def test_grouped_workload_dispatch_every_row(grouped):
+    """Every grouped row of the bf16 dispatch against the oracle's dispatch
+    of the same tokens, chunk by chunk; the chunks' rows cover all R rows
+    exactly once."""
+    G = grouped
+    w, R = G["w"], G["R"]
+    x = W.make_x(w, device=DEV)
     say("grouped workload: dispatch")
-    recv = ep().ep_dispatch(x, L, rows=ep().EP_ROWS_GROUP)
-    n = R["n_rows"]
-    gen = np.random.default_rng(0)
-    rows = np.concatenate([[0, n - 1], gen.choice(n, 3000, replace=False)])
-    rsel = torch.from_numpy(rows).to(DEV)
-    got = u16(recv.index_select(0, rsel))
-    src = torch.from_numpy(R["src"][rows]).to(DEV)
-    want = u16(x.index_select(0, src))
-    assert np.array_equal(got, want)
-    del recv
-    say("grouped workload: combine")
+    recv = ep().ep_dispatch(x, G["L"], rows=ep().EP_ROWS_GROUP)
+    torch.cuda.synchronize()
+    grow = R["grow"]
+    covered = 0
+    for t0 in range(0, w.T, CHUNK):
+        t1 = min(t0 + CHUNK, w.T)
+        used, dest = _chunk_slots(grow[t0:t1])
+        want = O.dispatch_bf16(u16(x[t0:t1]), dest, len(used))
+        got = u16(recv.index_select(0, torch.from_numpy(used).to(DEV)))
+        assert np.array_equal(got, want), (t0, t1)
+        covered += len(used)
+    assert covered == R["n_rows"]
+    del recv, x
+
+
+def test_grouped_workload_combine_every_token(grouped):
+    """Every token's grouped combine (within-group, then across groups in
+    group order) against the oracle, chunk by chunk."""
+    G = grouped
+    w, R = G["w"], G["R"]
     y = W.make_y(w, device=DEV)
-    out = ep().ep_combine(y, L, d_wt, d_idx, order=ep().EP_COMBINE_GROUPED)
-    toks = np.concatenate([[0, w.T - 1], gen.choice(w.T, 600, replace=False)])
-    slot_s = R["slot"][toks]
-    used = np.unique(slot_s[slot_s >= 0])
-    remap = -np.ones(R["n_sel"] + 1, np.int64)
-    remap[used] = np.arange(len(used))
-    slot_r = np.where(slot_s >= 0, remap[np.maximum(slot_s, 0)], -1)
-    ysub = u16(y.index_select(0, torch.from_numpy(used).to(DEV)))
-    want = O.combine_grouped(ysub, idx.numpy()[toks], slot_r, wt.numpy()[toks], w.E, w.G)
-    got = u16(out.index_select(0, torch.from_numpy(toks).to(DEV)))
-    assert np.array_equal(got, want)
+    say("grouped workload: combine")
+    out = ep().ep_combine(y, G["L"], G["d_wt"], G["d_idx"], order=ep().EP_COMBINE_GROUPED)
+    torch.cuda.synchronize()
+    idx, wt = G["idx"].numpy(), G["wt"].numpy()
+    for t0 in range(0, w.T, CHUNK):
+        t1 = min(t0 + CHUNK, w.T)
+        used, slot_r = _chunk_slots(R["slot"][t0:t1])
+        ysub = u16(y.index_select(0, torch.from_numpy(used).to(DEV)))
+        want = O.combine_grouped(ysub, idx[t0:t1], slot_r, wt[t0:t1], w.E, w.G)
+        assert np.array_equal(u16(out[t0:t1]), want), (t0, t1)
+    del y, out
 
 
 @pytest.mark.parametrize("mask_p", [0.0, 0.5])

@@ -85,7 +85,7 @@ struct BfVec<1> {
 template <int KMAX>
 struct Sel {
   int nv;           // number of valid selections
-  int os[KMAX];     // receive rows; entries past nv repeat the first row
+  int os[KMAX];     // receive rows; entries past nv repeat a valid row
   float ow[KMAX];   // weights
   bool newg[KMAX];  // position i starts a new group (never position 0)
 };
@@ -165,13 +165,15 @@ __device__ __forceinline__ void reduce_chunk(const CombineArgs& a, int64_t t,
   V bias[U][2];
   // Each row is a buffer resource with a wave-uniform base (scalar
   // registers); the in-row byte offset is one 32-bit vector register shared
-  // by all K loads.  A row is H * 2 < 2^32 bytes.
+  // by all K loads.  A row is H * 2 < 2^32 bytes.  A position past the valid
+  // count gets a zero-length resource: its load returns zeros without a
+  // memory access, and the reduction never reads it.
   const uint32_t row_bytes = static_cast<uint32_t>(nvec) * static_cast<uint32_t>(sizeof(V));
   __amdgpu_buffer_rsrc_t rows[KMAX];
 #pragma unroll
   for (int i = 0; i < KMAX; ++i)
     rows[i] = buffer_rsrc(reinterpret_cast<const char*>(yv) + static_cast<int64_t>(m.os[i]) * row_bytes,
-                          row_bytes);
+                          FULL || i < m.nv ? row_bytes : 0u);
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int vi = min(vb + u * kWave + lane, nvec - 1);

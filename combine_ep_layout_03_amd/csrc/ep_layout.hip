@@ -170,8 +170,6 @@ __global__ __launch_bounds__(kCountThreads) void k_layout_count(
   const int pb0 = blockIdx.x * chunk;
   const int nsub = min(chunk, nblocks - pb0);
   const int nwords = HALF ? (nsub * ncols + 1) / 2 : nsub * ncols;
-  for (int c = threadIdx.x; c < nwords; c += kCountThreads) hist[c] = 0;
-  __syncthreads();
   const bool lanes = GROUPED && kWave % K == 0;  // a token's entries in neighbouring lanes
   const bool small_g = E / epg <= 32;
   const float inv_epg = 1.0f / static_cast<float>(epg);
@@ -182,11 +180,12 @@ __global__ __launch_bounds__(kCountThreads) void k_layout_count(
   const uint32_t first = static_cast<uint32_t>(pb0) << span_shift;
   const uint32_t count = static_cast<uint32_t>(nsub) << span_shift;  // may pass n
   const int per = n == 0 ? 0 : static_cast<int>((count + kCountThreads - 1) / kCountThreads);
-  for (int j0 = 0; j0 < per; j0 += kCountBatch) {
-    // all loads of the batch first (out-of-range lanes read index 0), the
-    // out-of-range test only where the value is used, so no load waits for
-    // the one before it
-    int64_t v[kCountBatch];
+  // all loads of a batch first (out-of-range lanes read index 0), the
+  // out-of-range test only where the value is used, so no load waits for
+  // the one before it; the first batch is in flight while the histograms
+  // are cleared (the barrier waits for LDS work only)
+  int64_t v[kCountBatch];
+  auto load_batch = [&](int j0) {
 #pragma unroll
     for (int u = 0; u < kCountBatch; ++u) {
       v[u] = -1;
@@ -196,6 +195,12 @@ __global__ __launch_bounds__(kCountThreads) void k_layout_count(
         v[u] = idx[ok ? first + off : 0];  // n >= 1: index 0 is in bounds
       }
     }
+  };
+  load_batch(0);
+  for (int c = threadIdx.x; c < nwords; c += kCountThreads) hist[c] = 0;
+  __syncthreads();
+  for (int j0 = 0; j0 < per; j0 += kCountBatch) {
+    if (j0 > 0) load_batch(j0);
 #pragma unroll
     for (int u = 0; u < kCountBatch; ++u) {
       if (j0 + u < per) {  // block-uniform

@@ -92,6 +92,15 @@ def test_layout_workloads(name):
         (2000, 4, 1000, 0, 0.0),  # E near the key limit
         (2000, 4, 1024, 0, 0.0),  # E + G at the key limit
         (2000, 4, 992, 32, 0.1),  # E + G at the key limit, grouped
+        # count-block geometry: 16-bit tallies (1025 tally columns, more
+        # entries than 32-bit tallies admit), K not dividing a wave
+        (20000, 7, 992, 32, 0.1),
+        # 16-bit tallies with the lane test (K = 8, 8 groups), 512 place blocks
+        (16384, 8, 1016, 8, 0.05),
+        # 16 rounds per place block, 30 count blocks, 17 tally columns
+        (300000, 4, 16, 0, 0.1),
+        # K = 16: a token fills a 16-lane row; group bits by row shifts
+        (3000, 16, 256, 16, 0.1),
     ],
 )
 def test_layout_edge_shapes(T, K, E, G, mask):

@@ -310,14 +310,48 @@ def time_tiny(ep, W, dev, stream, reps):
     row_expert = torch.repeat_interleave(torch.arange(w.E, device=dev), L.counts.long())
     y = W.tiny_expert_outputs(recv[:n_sel], row_expert)
     out = torch.empty(w.T, w.H, dtype=torch.bfloat16, device=dev)
-    res = {"selections": int(n_sel)}
+    res = {"selections": int(n_sel),
+           "_note": "per call: one host launch per timed call, so mostly the host's launch path; "
+                    "graph_us: 32 calls captured in one HIP graph and replayed, the GPU time per call"}
     for name, fn in (
         ("layout", lambda: ep.ep_layout(d_idx, w.E, out=L)),
         ("dispatch_bf16", lambda: ep.ep_dispatch(x, L, out=recv)),
         ("combine", lambda: ep.ep_combine(y, L, d_wt, out=out)),
     ):
         res[name] = us_stats(per_call_us(fn, reps, stream))
+        res[name]["graph_us"] = round(graph_per_call_us(fn, 32, max(5, reps // 20), dev), 2)
     return res
+
+
+def graph_per_call_us(fn, calls, replays, dev):
+    """GPU time per call of `fn`: `calls` calls captured back to back in one
+    HIP graph, the graph replayed `replays` times between two events, so no
+    host work sits between the kernels."""
+    import torch
+
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        fn()  # warm the allocator and the library on the capture stream
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(replays):
+        g.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / (replays * calls)
+    del g
+    return us
 
 
 def time_mid(ep, W, dev, stream, reps, flush):

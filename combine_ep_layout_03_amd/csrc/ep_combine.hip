@@ -235,6 +235,10 @@ template <int KMAX, int VE, bool GROUPED, int U, int NB>
 __global__ __launch_bounds__(kBlock) void k_combine(CombineArgs a, int nchunks, int64_t items) {
   using B = BfVec<VE>;
   using V = typename B::V;
+  // The generation check, the slot load and the weight load run in sequence.
+  // Issuing all three at once (two round trips fewer per wave) measured
+  // slower at hidden 7168, top-8 of 256: flat 177 -> 182 us, grouped order
+  // over 65,536 tokens 1442 -> 1571 us.
   if (!layout_current(a.status, a.generation)) return;  // stale handle: write nothing
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t nw = grid_waves();

@@ -24,11 +24,13 @@ namespace ep {
 namespace {
 
 // Destination rows of token t, wave-uniform (scalar registers).  With
-// `dedup`, later k that repeat an earlier row are dropped.
+// `dedup`, later k that repeat an earlier row are dropped.  dest_lane issues
+// the load (lane k holds row k); spread_dests waits for it and spreads it.
+__device__ __forceinline__ int dest_lane(const ScatterArgs& a, int64_t t, int lane) {
+  return lane < a.K ? a.dest[t * a.K + lane] : -1;
+}
 template <int KMAX>
-__device__ __forceinline__ void load_dests(const ScatterArgs& a, int64_t t, int lane,
-                                           int (&d)[KMAX]) {
-  const int dl = lane < a.K ? a.dest[t * a.K + lane] : -1;
+__device__ __forceinline__ void spread_dests(const ScatterArgs& a, int dl, int (&d)[KMAX]) {
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) d[j] = readlane(dl, j);
   if (a.dedup) {
@@ -39,6 +41,11 @@ __device__ __forceinline__ void load_dests(const ScatterArgs& a, int64_t t, int 
         if (d[j] == d[jj]) d[j] = -1;
     }
   }
+}
+template <int KMAX>
+__device__ __forceinline__ void load_dests(const ScatterArgs& a, int64_t t, int lane,
+                                           int (&d)[KMAX]) {
+  spread_dests<KMAX>(a, dest_lane(a, t, lane), d);
 }
 
 // Has the token any destination row?  (Wave-uniform: d is.)  A token
@@ -55,7 +62,6 @@ template <int KMAX, int VB, int U>
 __global__ __launch_bounds__(kBlock) void k_scatter_bf16(ScatterArgs a, int nchunks,
                                                          int64_t items) {
   using V = typename VecOf<VB>::type;
-  if (!dispatch_may_write(a)) return;  // stale layout or overflow: write nothing
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t nw = grid_waves();
   const int64_t row_bytes = static_cast<int64_t>(a.H) * 2;
@@ -64,7 +70,17 @@ __global__ __launch_bounds__(kBlock) void k_scatter_bf16(ScatterArgs a, int nchu
   int d[KMAX];
   int64_t loaded = -1;
   bool any = false;
-  for (int64_t it = global_wave(); it < items; it += nw) {
+  // The first token's destination rows and the gate words load together.
+  const int64_t it0 = global_wave();
+  const int64_t t0 = it0 < items ? it0 / nchunks : 0;
+  const int dl0 = it0 < items ? dest_lane(a, t0, lane) : -1;
+  if (!dispatch_may_write(a, dispatch_gate(a))) return;  // stale layout or overflow: write nothing
+  if (it0 < items) {
+    spread_dests<KMAX>(a, dl0, d);
+    any = any_dest<KMAX>(d);
+    loaded = t0;
+  }
+  for (int64_t it = it0; it < items; it += nw) {
     const int64_t t = it / nchunks;
     const int c = static_cast<int>(it - t * nchunks);
     if (t != loaded) {
@@ -116,11 +132,14 @@ template <int KMAX, bool ROWBUF>
 __global__ __launch_bounds__(kBlock) void k_scatter_fp8(ScatterArgs a, int64_t row_bytes) {
   constexpr int kMaxScaleSlots = 4;  // H <= 4 * 64 * 128
   constexpr int kRowSteps = 8;       // ROWBUF: H <= 8 * 1024
-  if (!dispatch_may_write(a)) return;
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t nw = grid_waves();
   int64_t t = global_wave();
-  if (t >= a.T) return;
+  // the first token's destination rows and the gate words load together
+  const int dl0 = t < a.T ? dest_lane(a, t, lane) : -1;
+  if (!dispatch_may_write(a, dispatch_gate(a)) || t >= a.T) return;
+  int d[KMAX];
+  spread_dests<KMAX>(a, dl0, d);
   const int H = a.H;
   const int ngroups = H / 128;
   const int nsteps = (H + kWave * 16 - 1) / (kWave * 16);
@@ -180,9 +199,8 @@ __global__ __launch_bounds__(kBlock) void k_scatter_fp8(ScatterArgs a, int64_t r
     return q;
   };
   bool have0 = false;  // step 0 of token t is loaded (by the previous token's last step)
-  for (; t < a.T; t += nw) {
-    int d[KMAX];
-    load_dests<KMAX>(a, t, lane, d);
+  for (bool first = true; t < a.T; t += nw, first = false) {
+    if (!first) load_dests<KMAX>(a, t, lane, d);
     if (!any_dest<KMAX>(d)) {
       have0 = false;
       continue;

@@ -57,13 +57,27 @@ constexpr int kStatusDispatchOverflow = 7;
 constexpr int kStatusGeneration = 8;
 constexpr int kStatusStale = 9;
 
+// A status word read through the vector memory path.  Scalar loads return
+// out of order, so any later wait for a kernel argument would also wait for
+// this word; vector loads retire in order, so the loads issued after it
+// (a wave's first indices) stay in flight while it is checked.
+__device__ __forceinline__ int32_t status_word(const int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Is the layout behind `status` still the one the caller's handle names?
-// Wave-uniform (one word, read by every lane).  On a stale handle the grid's
-// first lane sets the sticky stale flag; the caller's kernel then returns.
-__device__ __forceinline__ bool layout_current(int32_t* status, uint32_t generation) {
-  const bool cur = static_cast<uint32_t>(status[kStatusGeneration]) == generation;
+// `word` is status[kStatusGeneration] as the wave read it (the scatters load
+// it together with their first destination rows, so the check costs them no
+// round trip of its own).  On a stale handle the grid's first lane sets the
+// sticky stale flag; the caller's kernel then returns.
+__device__ __forceinline__ bool layout_current(int32_t* status, int32_t word,
+                                               uint32_t generation) {
+  const bool cur = static_cast<uint32_t>(word) == generation;
   if (!cur && blockIdx.x == 0 && threadIdx.x == 0) status[kStatusStale] = 1;
   return cur;
+}
+__device__ __forceinline__ bool layout_current(int32_t* status, uint32_t generation) {
+  return layout_current(status, status[kStatusGeneration], generation);
 }
 
 struct ScatterArgs {
@@ -88,14 +102,28 @@ struct ScatterArgs {
 // and both base alignments.
 hipError_t launch_scatter_bf16(const ScatterArgs& a, int vec_bytes, hipStream_t s);
 
+// The two device words a dispatch kernel checks before its first store,
+// loaded together and early (the loads of the first token's destination
+// rows follow without waiting for them).
+struct DispatchGate {
+  int32_t generation;
+  int32_t rows_needed;
+};
+__device__ __forceinline__ DispatchGate dispatch_gate(const ScatterArgs& a) {
+  return {status_word(a.status + kStatusGeneration), status_word(a.rows_needed)};
+}
 // May a dispatch kernel write?  Only if the layout is current and its rows
 // fit the capacity (an overflow writes no row).  The grid's first lane
-// records the overflow verdict of a current call (1 or 0).
-__device__ __forceinline__ bool dispatch_may_write(const ScatterArgs& a) {
-  if (!layout_current(a.status, a.generation)) return false;
-  const bool fits = static_cast<int64_t>(*a.rows_needed) <= a.capacity;
+// records the overflow verdict of a current call (1 or 0).  Every wave
+// calls this before any store.
+__device__ __forceinline__ bool dispatch_may_write(const ScatterArgs& a, const DispatchGate& g) {
+  if (!layout_current(a.status, g.generation, a.generation)) return false;
+  const bool fits = static_cast<int64_t>(g.rows_needed) <= a.capacity;
   if (blockIdx.x == 0 && threadIdx.x == 0) a.status[kStatusDispatchOverflow] = fits ? 0 : 1;
   return fits;
+}
+__device__ __forceinline__ bool dispatch_may_write(const ScatterArgs& a) {
+  return dispatch_may_write(a, dispatch_gate(a));
 }
 // packed fp8 rows; H % 128 == 0, H <= 32768, 16-byte aligned bases and stride.
 hipError_t launch_scatter_fp8(const ScatterArgs& a, int64_t row_bytes, hipStream_t s);

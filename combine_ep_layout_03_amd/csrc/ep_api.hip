@@ -3,6 +3,7 @@
 #include <limits.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 
@@ -201,6 +202,10 @@ int ep_dispatch(const ep_problem_t* p, const ep_layout_t* L, const void* x, void
   int vb = 16;
   if (format == EP_FORMAT_FP8_PACKED) {
     if (!aligned(x, 16) || !aligned(recv, 16) || stride % 16 != 0) return EP_EINVAL;
+    // Rows on 128-byte lines: extend each row with zeros to its line end, so
+    // no line is written in part (the row format's own zero padding, longer).
+    if (aligned(recv, 128) && stride % 128 == 0)
+      row_bytes = std::min(stride, (row_bytes + 127) / 128 * 128);
     err = ep::launch_scatter_fp8(a, row_bytes, stream);
   } else {
     vb = vec_bytes_for(row_bytes, x, recv);

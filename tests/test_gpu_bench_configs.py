@@ -100,6 +100,8 @@ def test_dispatch_fp8_grouped_rows_full_size(pages):
     want = O.dispatch_fp8(u16(P["x"]), RO["grow"], R)
     got = recv[:R, :rb].cpu().numpy()
     assert np.array_equal(got, want)
+    # 7424-byte pitch: each row is zero-filled from its end to its 128-byte line end
+    assert bool((recv[:R, rb:] == 0).all())
 
 
 def test_dispatch_fp8_align128_zero_padding_full_size(pages):
@@ -118,6 +120,8 @@ def test_dispatch_fp8_align128_zero_padding_full_size(pages):
     want = O.dispatch_fp8(u16(P["x"]), RO["slot"], n_al)
     got = recv[:n_al, :rb].cpu().numpy()
     assert np.array_equal(got, want)
+    # selections and padding rows alike are zero-filled to the 7424-byte line end
+    assert bool((recv[:n_al, rb:] == 0).all())
     # rows past the layout's rows are never touched
     assert bool((recv[n_al:] == 0xA5).all())
 

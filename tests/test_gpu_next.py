@@ -54,16 +54,19 @@ def test_alignment_zero_padding(A, fp8):
     if fp8:
         rb = O.fp8_row_bytes(w.H)
         want = O.dispatch_fp8(u16(x), R["slot"], n)
-        for zp in (True, False):
-            out = torch.full((L.max_expert_rows(), rb), 0xC3, dtype=torch.uint8, device=DEV)
-            ep().ep_dispatch(x.to(DEV), L, fp8=True, out=out, zero_padding=zp)
-            got = out.cpu().numpy()
-            assert np.array_equal(got[:n][~pad], want[~pad])
-            if zp:
-                assert np.array_equal(got[:n][pad], want[pad]) and not got[:n][pad].any()
-            else:
-                assert (got[:n][pad] == 0xC3).all()
-            assert (got[n:] == 0xC3).all()
+        # packed rows, then rows on a 128-byte pitch (zero-filled to the line end)
+        for pitch in (rb, (rb + 127) // 128 * 128):
+            for zp in (True, False):
+                out = torch.full((L.max_expert_rows(), pitch), 0xC3, dtype=torch.uint8, device=DEV)
+                ep().ep_dispatch(x.to(DEV), L, fp8=True, out=out, zero_padding=zp)
+                got = out.cpu().numpy()
+                assert np.array_equal(got[:n, :rb][~pad], want[~pad])
+                assert not got[:n, rb:][~pad].any()
+                if zp:
+                    assert np.array_equal(got[:n, :rb][pad], want[pad]) and not got[:n][pad].any()
+                else:
+                    assert (got[:n][pad] == 0xC3).all()
+                assert (got[n:] == 0xC3).all()
     else:
         want = O.dispatch_bf16(u16(x), R["slot"], n)
         for zp in (True, False):

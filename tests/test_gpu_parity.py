@@ -295,9 +295,21 @@ def test_dispatch_poison_and_capacity():
     assert bool((out3 == 0xAB).all())
 
 
-@pytest.mark.parametrize("fp8,H,pitch", [(True, 7168, 7424), (True, 128, 256), (True, 384, 416), (False, 136, 512), (False, 9, 20)])
+def fp8_line_fill_end(rb: int, pitch: int, base_ptr: int) -> int:
+    """Where ep_dispatch's fp8 zero fill ends inside a row: the next 128-byte
+    boundary when the receive base and the pitch are both multiples of 128
+    (never past the pitch), otherwise the packed row's own end."""
+    if base_ptr % 128 == 0 and pitch % 128 == 0:
+        return min(pitch, (rb + 127) // 128 * 128)
+    return rb
+
+
+@pytest.mark.parametrize("fp8,H,pitch", [(True, 7168, 7424), (True, 128, 256), (True, 128, 384), (True, 384, 416),
+                                         (False, 136, 512), (False, 9, 20)])
 def test_dispatch_row_pitch(fp8, H, pitch):
-    """Rows at a padded pitch: row bytes equal the oracle's, gap bytes untouched."""
+    """Rows at a padded pitch: row bytes equal the oracle's; fp8 rows on
+    128-byte lines are zero-filled to their line end; every other gap byte
+    is untouched."""
     say("dispatch pitch", fp8, H, pitch)
     w = W.Workload("pitch", T=700 if H > 1000 else 1500, H=H, K=8, E=64, mask_p=0.1, seed=H + pitch)
     idx, _ = W.make_routing(w)
@@ -310,10 +322,13 @@ def test_dispatch_row_pitch(fp8, H, pitch):
         rb = O.fp8_row_bytes(H)
         out = torch.full((cap, pitch), 0xA5, dtype=torch.uint8, device=DEV)
         ep().ep_dispatch(x.to(DEV), L, fp8=True, out=out)
+        fe = fp8_line_fill_end(rb, pitch, out.data_ptr())
+        assert fe == (rb if pitch % 128 else min(pitch, (rb + 127) // 128 * 128))  # torch bases are 128-aligned
         got = out.cpu().numpy()
         want = O.dispatch_fp8(u16(x), R["slot"], n)
         assert np.array_equal(got[:n, :rb], want)
-        assert (got[:n, rb:] == 0xA5).all() and (got[n:] == 0xA5).all()
+        assert (got[:n, rb:fe] == 0).all()
+        assert (got[:n, fe:] == 0xA5).all() and (got[n:] == 0xA5).all()
     else:
         out = torch.full((cap, pitch // 2), -23131, dtype=torch.int16, device=DEV)  # 0xA5A5
         ep().ep_dispatch(x.to(DEV), L, out=out.view(torch.bfloat16))

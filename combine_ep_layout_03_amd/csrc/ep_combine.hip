@@ -273,14 +273,17 @@ hipError_t combine_v(const CombineArgs& a, hipStream_t s) {
   const int nvec = a.H / VE;
   const int nchunks = (nvec + kWave * U - 1) / (kWave * U);
   const int64_t items = a.T * nchunks;
-  // The flat order runs best with at most 5 of its blocks on a CU: each
-  // block asks for 29 KiB of LDS it does not use, so 5 fit in a CU's 160 KiB
-  // and 6 do not.  Hidden 7168, top-8 of 256: 178.5 us at 5 waves per SIMD,
-  // 181.5 at 6, 183.2 at the 8 its registers allow; the grouped order is best
-  // uncapped (4 waves per SIMD: 1528 against 1437 us at 65,536 tokens).
-  constexpr size_t kOccupancyLds = GROUPED ? 0 : 29696;
+  // With 8 or more rows per token the flat order runs best with at most 5
+  // of its blocks on a CU: each block asks for 29 KiB of LDS it does not
+  // use, so 5 fit in a CU's 160 KiB and 6 do not.  Hidden 7168, top-8 of 256:
+  // 178.5 us at 5 waves per SIMD, 181.5 at 6, 183.2 at the 8 its registers
+  // allow.  With fewer rows per token fewer rows are open per wave, and the
+  // cap costs: hidden 4096, top-4 of 64, 4096 tokens, cold caches: 35.7 us
+  // capped, 33.0 uncapped.  The grouped order is best uncapped (4 waves per
+  // SIMD: 1528 against 1437 us at 65,536 tokens).
+  const size_t occupancy_lds = !GROUPED && a.K >= 8 ? 29696 : 0;
   constexpr auto kern = k_combine<KMAX, VE, GROUPED, U, NB>;
-  kern<<<wave_per_item_blocks(items), kBlock, kOccupancyLds, s>>>(a, nchunks, items);
+  kern<<<wave_per_item_blocks(items), kBlock, occupancy_lds, s>>>(a, nchunks, items);
   return hipGetLastError();
 }
 

@@ -32,10 +32,11 @@ def u16(t):
     return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
 
 
-@pytest.mark.parametrize("A", [2, 4, 64, 128])
+@pytest.mark.parametrize("A,T", [(2, 1200), (4, 1200), (64, 1200), (128, 1200), (16, 200)])
 @pytest.mark.parametrize("fp8", [False, True])
-def test_alignment_zero_padding(A, fp8):
-    w = W.by_name("skewed_masked").replace(T=1200, H=256 if fp8 else 200, seed=A)
+def test_alignment_zero_padding(A, T, fp8):
+    # T = 200: 1600 entries, laid out by one fused block
+    w = W.by_name("skewed_masked").replace(T=T, H=256 if fp8 else 200, seed=A)
     print("alignment", A, fp8, flush=True)
     idx, _ = W.make_routing(w)
     x = W.make_x(w)
@@ -97,9 +98,10 @@ def test_expert_row_list_overflow():
     assert L2.status[ep().EP_STATUS_EXPERT_LIST_OVERFLOW].item() == 1
 
 
-def test_cumulative_recv_stats():
+@pytest.mark.parametrize("T", [3000, 150])  # two launches; one fused block
+def test_cumulative_recv_stats(T):
     """Three accumulating layouts with a quarter of the selections masked."""
-    w = W.by_name("pages").replace(T=3000, mask_p=0.25)
+    w = W.by_name("pages").replace(T=T, mask_p=0.25)
     stats = torch.zeros(w.E, dtype=torch.int32, device=DEV)
     want = np.zeros(w.E, np.int64)
     for s in range(3):

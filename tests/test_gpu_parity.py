@@ -101,6 +101,14 @@ def test_layout_workloads(name):
         (300000, 4, 16, 0, 0.1),
         # K = 16: a token fills a 16-lane row; group bits by row shifts
         (3000, 16, 256, 16, 0.1),
+        # up to 2048 entries one block tallies and places everything (1, 2,
+        # 4 and 8 rounds); 2056 entries is the first two-launch size
+        (32, 8, 64, 8, 0.1),
+        (33, 8, 64, 8, 0.1),
+        (100, 7, 48, 6, 0.2),
+        (256, 8, 1016, 8, 0.05),
+        (682, 3, 100, 0, 0.3),
+        (257, 8, 256, 0, 0.1),
     ],
 )
 def test_layout_edge_shapes(T, K, E, G, mask):
@@ -115,9 +123,10 @@ def test_layout_edge_shapes(T, K, E, G, mask):
     check_layout(L, R, E, G)
 
 
-def test_layout_invalid_and_duplicate_ids():
+@pytest.mark.parametrize("T", [3000, 200])  # two launches; one fused block
+def test_layout_invalid_and_duplicate_ids(T):
     g = torch.Generator().manual_seed(11)
-    T, K, E = 3000, 8, 64
+    K, E = 8, 64
     idx = torch.randint(-3, E + 3, (T, K), generator=g)  # -3,-2,E.. invalid; duplicates allowed
     wt = torch.rand(T, K, generator=g)
     for G in (0, 8):

@@ -3,14 +3,15 @@
 // Each row is stored once, at the expert-major destination the layout gave
 // it (base of its destination + claimed slot), so no compaction pass runs
 // afterwards (TileScale PR #68, "EP v2 intranode dispatch/combine": PR
-// summary and Design section).  Here a token row is cut into
-// chunks; the grid's waves take the (token, chunk) items cyclically, read
-// each chunk of the source row once and store it once per destination row.  Receive rows are written with non-temporal stores: they
-// are not read again by this step and streaming them past the caches
-// measured about 15-20% faster on MI355X than ordinary stores.  Vectors are 16
-// bytes when the row size and base alignment allow, otherwise the widest
-// vector dividing both, so there is no remainder to drop (the pages'
-// copy-tail fix, commit on cp_warp_impl).
+// summary and Design section).  Here a token row is cut into chunks; the
+// grid's waves take the (token, chunk) items cyclically, read each chunk of
+// the source row once and store it once per destination row.  Receive rows
+// are written with non-temporal stores: they are not read again by this
+// step and streaming them past the caches measured about 15-20% faster on
+// MI355X than ordinary stores.  Vectors are 16 bytes when the row size and
+// base alignment allow, otherwise the widest vector dividing both, so there
+// is no remainder to drop (the pages' copy-tail fix, commit on
+// cp_warp_impl).
 //
 // The fp8 variant fuses DeepEP's per-token, per-128-element cast into the
 // same pass and writes payload, scales and padding of the packed row in one
@@ -127,9 +128,9 @@ __global__ __launch_bounds__(kBlock) void k_scatter_bf16(ScatterArgs a, int nchu
 // With ROWBUF (H <= 8192) the token's whole payload stays in registers too,
 // and each destination row is then written in one burst: payload, scales,
 // padding.  Otherwise each step's payload is stored as it is made and the
-// scales follow the last step (the launcher picks by row pitch).  Writing the scales piecewise per step, or
-// at the packed 7392-byte pitch instead of a 128-byte aligned one, measured
-// 20-45% slower at hidden 7168.
+// scales follow the last step (the launcher picks by row pitch).  Writing
+// the scales piecewise per step, or at the packed 7392-byte pitch instead of
+// a 128-byte aligned one, measured 20-45% slower at hidden 7168.
 template <int KMAX, bool ROWBUF>
 __global__ __launch_bounds__(kBlock) void k_scatter_fp8(ScatterArgs a, int64_t row_bytes) {
   constexpr int kMaxScaleSlots = 4;  // H <= 4 * 64 * 128

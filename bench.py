@@ -60,8 +60,9 @@ def counted_traffic(op, workload):
 
 def time_extras(ep, W, w, d_idx, d_wt, x, y, L, n_sel, rb, pitch, reps, only=None, flush=None):
     """Each op beside the headline step, timed alone (back to back, HIP
-    events on the current stream) at the same 8192 x 7168 workload:
-    grouped-order combine over 8 groups of 32 experts, the grouped (deduped)
+    events on the current stream) at the same 8192 x 7168 workload: the
+    plain bf16 dispatch, grouped-order combine over 8 groups of 32 experts,
+    the grouped (deduped)
     fp8 dispatch, dispatch into 128-row-aligned expert segments with zeroed
     padding, combine seeded by two bias rows, and the layout with
     receive-stats accumulation, the grouped GEMM consumer (plain weights,
@@ -85,6 +86,7 @@ def time_extras(ep, W, w, d_idx, d_wt, x, y, L, n_sel, rb, pitch, reps, only=Non
     out = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
     recv_g = torch.empty(max(R, 1), pitch, dtype=torch.uint8, device=dev)
     recv_a = torch.empty(LA.max_expert_rows(), pitch, dtype=torch.uint8, device=dev)
+    recv_b = torch.empty(max(n_sel, 1), H, dtype=torch.bfloat16, device=dev)
     g = torch.Generator(device=dev)
     g.manual_seed(77)
     b0 = torch.randn(T, H, generator=g, device=dev).to(torch.bfloat16)
@@ -92,6 +94,11 @@ def time_extras(ep, W, w, d_idx, d_wt, x, y, L, n_sel, rb, pitch, reps, only=Non
     stats = torch.zeros(E, dtype=torch.int32, device=dev)
     comb_b = n_sel * H * 2 + T * K * 8 + T * H * 2
     cases = {
+        # the plain bf16 row scatter (no quantisation) of the same step
+        "dispatch_bf16": (
+            lambda: ep.ep_dispatch(x, L, out=recv_b, capacity=n_sel),
+            T * H * 2 + T * K * 4 + n_sel * H * 2,
+        ),
         "combine_grouped_g8": (
             lambda: ep.ep_combine(y, LG, d_wt, d_idx, order=ep.EP_COMBINE_GROUPED, out=out),
             comb_b + T * K * 8,

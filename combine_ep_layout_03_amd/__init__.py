@@ -390,7 +390,10 @@ def ep_dispatch(
     with ``fp8``.  The receive-row pitch is the row size of ``out`` (one row
     of the 2-D tensor per receive row); when ``out`` is allocated here it is
     ``row_stride`` bytes (default: the row size, rows packed back to back).
-    Only the first row-size bytes of each row are written.  The default
+    Only the first row-size bytes of each row are written, except that fp8
+    rows on 128-byte lines (``out`` and the pitch multiples of 128 bytes,
+    as with ``fp8_row_pitch``) are zero-filled from their end to the next
+    128-byte boundary, so every line is written whole.  The default
     capacity is the worst case (T*K expert rows, min(T*G, T*K) group rows),
     so no host synchronisation is needed.  With a smaller ``capacity`` the
     rows needed may exceed it: the call then writes no row and sets the

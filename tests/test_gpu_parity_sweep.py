@@ -64,8 +64,10 @@ def test_parity_sweep(seed, n, wide):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     cases = _wide_cases(n, seed) if wide else rs._cases(n=n, seed=seed)
-    for c in cases:
+    for i, c in enumerate(cases):
         rs.test_random_shape_matches_oracle(c)
+        if (i + 1) % 200 == 0:
+            print(f"seed {seed}: {i + 1} shapes match", flush=True)
     print(f"seed {seed}: {len(cases)} shapes match the oracle", flush=True)
 
 

@@ -526,6 +526,54 @@ int main(void) {
     hipFree(d_yp);
   }
 
+  /* the allocation-free layout (no workspace argument) gives the same
+     counts, offsets, slots and status words as ep_layout */
+  {
+    int32_t *d_counts2, *d_offsets2, *d_slot2, *d_status2;
+    static int32_t counts2[E], offsets[E + 1], offsets2[E + 1], slot2[T * K], st1[EP_STATUS_WORDS],
+        st2[EP_STATUS_WORDS];
+    ep_layout_t L2;
+    CHECK_HIP(hipMalloc((void**)&d_counts2, E * 4));
+    CHECK_HIP(hipMalloc((void**)&d_offsets2, (E + 1) * 4));
+    CHECK_HIP(hipMalloc((void**)&d_slot2, T * K * 4));
+    CHECK_HIP(hipMalloc((void**)&d_status2, EP_STATUS_WORDS * 4));
+    memset(&L2, 0, sizeof L2);
+    L2.counts = d_counts2;
+    L2.offsets = d_offsets2;
+    L2.slot = d_slot2;
+    L2.status = d_status2;
+    memset(&L, 0, sizeof L);
+    L.counts = d_counts;
+    L.offsets = d_offsets;
+    L.slot = d_slot;
+    L.status = d_status;
+    CHECK_EP(ep_layout(&p, d_idx, d_w, &L, d_ws, ws_bytes, s));
+    CHECK_EP(ep_layout_noalloc(&p, d_idx, d_w, &L2, s));
+    CHECK_HIP(hipStreamSynchronize(s));
+    CHECK_HIP(hipMemcpy(counts, d_counts, sizeof counts, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(counts2, d_counts2, sizeof counts2, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(offsets, d_offsets, sizeof offsets, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(offsets2, d_offsets2, sizeof offsets2, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(slot, d_slot, sizeof slot, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(slot2, d_slot2, sizeof slot2, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(st1, d_status, sizeof st1, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(st2, d_status2, sizeof st2, hipMemcpyDeviceToHost));
+    if (memcmp(counts, counts2, sizeof counts) || memcmp(offsets, offsets2, sizeof offsets) ||
+        memcmp(slot, slot2, sizeof slot)) {
+      printf("ep_layout_noalloc differs from ep_layout\n");
+      return 1;
+    }
+    for (e = 0; e < EP_STATUS_WORDS; ++e)
+      if (e != EP_STATUS_GENERATION && st1[e] != st2[e]) {
+        printf("ep_layout_noalloc status word %d: %d, ep_layout %d\n", e, st2[e], st1[e]);
+        return 1;
+      }
+    hipFree(d_counts2);
+    hipFree(d_offsets2);
+    hipFree(d_slot2);
+    hipFree(d_status2);
+  }
+
   hipFree(d_idx);
   hipFree(d_w);
   hipFree(d_x);
@@ -540,7 +588,7 @@ int main(void) {
   printf("OK: %d selections, %d invalid ids, combine of the dispatched rows = K_eff * x, "
          "fp8 rows exact, overflow and stale handles write nothing and are flagged, "
          "grouped rows, lists and grouped combine exact, "
-         "grouped GEMM exact (plain and packed weights)\n",
+         "grouped GEMM exact (plain and packed weights), allocation-free layout identical\n",
          n_sel, n_invalid);
   return 0;
 }

@@ -5,7 +5,7 @@ the unit-weight combine of the dispatched rows equal to K_eff * x, the packed
 fp8 rows byte for byte (scale 2^-6 and payload codes of 64 * x), grouped rows,
 their row lists and the grouped-order combine, and the grouped GEMM on small
 integers (plain and packed weights) equal to the bf16 rounding of the exact
-sums."""
+sums; and the allocation-free layout equal to ep_layout's."""
 import os
 import subprocess
 

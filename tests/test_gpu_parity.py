@@ -108,6 +108,8 @@ def test_layout_workloads(name):
         (100, 7, 48, 6, 0.2),
         (256, 8, 1016, 8, 0.05),
         (682, 3, 100, 0, 0.3),
+        (64, 32, 512, 16, 0.1),  # fused, K = 32: group tests by LDS permutes
+        (100, 13, 96, 8, 0.1),  # fused, K not dividing a wave: per-lane path
         (257, 8, 256, 0, 0.1),
     ],
 )

@@ -231,8 +231,9 @@ __device__ __forceinline__ void empty_chunk(const CombineArgs& a, int64_t t,
   }
 }
 
-template <int KMAX, int VE, bool GROUPED, int U, int NB>
-__global__ __launch_bounds__(kBlock) void k_combine(CombineArgs a, int nchunks, int64_t items) {
+// BT threads per block (256, or 64: one wave per block).
+template <int KMAX, int VE, bool GROUPED, int U, int NB, int BT>
+__global__ __launch_bounds__(BT) void k_combine(CombineArgs a, int nchunks, int64_t items) {
   using B = BfVec<VE>;
   using V = typename B::V;
   // The generation check, the slot load and the weight load run in sequence.
@@ -240,13 +241,16 @@ __global__ __launch_bounds__(kBlock) void k_combine(CombineArgs a, int nchunks, 
   // slower at hidden 7168, top-8 of 256: flat 177 -> 182 us, grouped order
   // over 65,536 tokens 1442 -> 1571 us.
   if (!layout_current(a.status, a.generation)) return;  // stale handle: write nothing
+  constexpr int kWaves = BT / kWave;
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t nw = grid_waves();
+  const int64_t nw = static_cast<int64_t>(gridDim.x) * kWaves;
   const int nvec = a.H / VE;
   const V* yv = static_cast<const V*>(a.y);
   Sel<KMAX> m;
   int64_t loaded = -1;
-  for (int64_t it = global_wave(); it < items; it += nw) {
+  const int64_t w0 = static_cast<int64_t>(blockIdx.x) * kWaves +
+                     (kWaves == 1 ? 0 : __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave));
+  for (int64_t it = w0; it < items; it += nw) {
     const int64_t t = it / nchunks;
     const int c = static_cast<int>(it - t * nchunks);
     if (t != loaded) {
@@ -274,16 +278,23 @@ hipError_t combine_v(const CombineArgs& a, hipStream_t s) {
   const int nchunks = (nvec + kWave * U - 1) / (kWave * U);
   const int64_t items = a.T * nchunks;
   // With 8 or more rows per token the flat order runs best with at most 5
-  // of its blocks on a CU: each block asks for 29 KiB of LDS it does not
-  // use, so 5 fit in a CU's 160 KiB and 6 do not.  Hidden 7168, top-8 of 256:
-  // 178.5 us at 5 waves per SIMD, 181.5 at 6, 183.2 at the 8 its registers
-  // allow.  With fewer rows per token fewer rows are open per wave, and the
-  // cap costs: hidden 4096, top-4 of 64, 4096 tokens, cold caches: 35.7 us
-  // capped, 33.0 uncapped.  The grouped order is best uncapped (4 waves per
-  // SIMD: 1528 against 1437 us at 65,536 tokens).
-  const size_t occupancy_lds = !GROUPED && a.K >= 8 ? 29696 : 0;
-  constexpr auto kern = k_combine<KMAX, VE, GROUPED, U, NB>;
-  kern<<<wave_per_item_blocks(items), kBlock, occupancy_lds, s>>>(a, nchunks, items);
+  // waves per SIMD: hidden 7168, top-8 of 256: 178.5 us at 5, 181.5 at 6,
+  // 183.2 at the 8 its registers allow.  The cap is unused LDS, and the
+  // blocks are single waves (8000 bytes each, 20 to a CU), so a finished
+  // wave frees its place at once instead of waiting for its block's other
+  // waves: 174.9 against 176.7 us with 4-wave blocks of 29 KiB, two biases
+  // 185.1 against 188.0 us.  With fewer rows per token fewer rows are open
+  // per wave, and the cap costs: hidden 4096, top-4 of 64, 4096 tokens, cold
+  // caches: 35.7 us capped, 33.0 uncapped.  The grouped order is best
+  // uncapped in 4-wave blocks (4 waves per SIMD: 1528 against 1437 us at
+  // 65,536 tokens; single-wave blocks 1474 us).
+  if (!GROUPED && a.K >= 8) {
+    constexpr auto kern = k_combine<KMAX, VE, GROUPED, U, NB, kWave>;
+    kern<<<wave_per_item_blocks(items, 1), kWave, 8000, s>>>(a, nchunks, items);
+  } else {
+    constexpr auto kern = k_combine<KMAX, VE, GROUPED, U, NB, kBlock>;
+    kern<<<wave_per_item_blocks(items), kBlock, 0, s>>>(a, nchunks, items);
+  }
   return hipGetLastError();
 }
 

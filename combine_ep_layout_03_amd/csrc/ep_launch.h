@@ -25,11 +25,11 @@ inline int64_t grid_override() {
 // Blocks that give each wave one of `items` work items (at least one block,
 // at most 2^24 - 1 so the grid's work-item count stays below 2^32; the
 // kernels walk their items cyclically, so a capped grid still covers them).
-inline unsigned wave_per_item_blocks(int64_t items) {
+inline unsigned wave_per_item_blocks(int64_t items, int waves_per_block = kWavesPerBlock) {
   const int64_t forced = grid_override();
   if (forced > 0) return static_cast<unsigned>(forced);
   constexpr int64_t kMaxBlocks = (1LL << 24) - 1;
-  int64_t b = (items + kWavesPerBlock - 1) / kWavesPerBlock;
+  int64_t b = (items + waves_per_block - 1) / waves_per_block;
   if (b < 1) b = 1;
   return static_cast<unsigned>(b < kMaxBlocks ? b : kMaxBlocks);
 }

@@ -283,7 +283,9 @@ hipError_t combine_v(const CombineArgs& a, hipStream_t s) {
   // blocks are single waves (8000 bytes each, 20 to a CU), so a finished
   // wave frees its place at once instead of waiting for its block's other
   // waves: 174.9 against 176.7 us with 4-wave blocks of 29 KiB, two biases
-  // 185.1 against 188.0 us.  With fewer rows per token fewer rows are open
+  // 185.1 against 188.0 us.  At 4 waves per SIMD (16 blocks of 10 KiB) the
+  // bench shape gains another 1.0 us but the skewed, masked routing loses
+  // 4.6 us (162.9 against 158.3), so 5 it stays.  With fewer rows per token fewer rows are open
   // per wave, and the cap costs: hidden 4096, top-4 of 64, 4096 tokens, cold
   // caches: 35.7 us capped, 33.0 uncapped.  The grouped order is best
   // uncapped in 4-wave blocks (4 waves per SIMD: 1528 against 1437 us at

@@ -7,9 +7,10 @@
 // multiply-add): acc starts at +0, each term is fl32(w * y) and each sum is
 // fl32(acc + term).  Flat order: ascending k.  Grouped order: the token's
 // rows inside one expert group are summed first in ascending k, then the
-// group partials in ascending group order, as the expanded combine sums a
-// token's local-expert rows before one row per destination is sent (commit
-// adding kDoExpandedSend).  Masked entries (-1) are skipped, so a fully
+// group partials in ascending group order: the order of the expanded
+// combine, which adds up the rows a token has on one destination's experts
+// before that destination's single row goes out (commit adding
+// kDoExpandedSend).  Masked entries (-1) are skipped, so a fully
 // masked token gives +0 (commit on masked topk_idx).  An optional bias (one
 // or two bf16 rows per token) seeds the accumulator instead of +0, so a fully
 // masked token returns its bias (commit adding receive stats and combine

@@ -6,10 +6,11 @@
  * intranode dispatch/combine":
  *   - dispatch counts each token's selections per destination, turns the
  *     counts into a base per destination, and writes every row straight to
- *     base + a claimed slot, its final compact index, so no copy epilogue
- *     runs afterwards (PR summary; PR description, Design section; commit
- *     adding DeepEP's do_expand, where the destination becomes the expert
- *     and the base is an exclusive prefix sum of per-expert counts);
+ *     base + a claimed slot, already its place in the dense receive buffer,
+ *     so no later pass moves rows (PR summary; PR description, Design
+ *     section; commit adding DeepEP's do_expand, where the destination
+ *     becomes the expert and the base is an exclusive prefix sum of
+ *     per-expert counts);
  *   - the fp8 payload is DeepEP's per-token, per-128-element cast, packed
  *     with its fp32 scales into one row moved by one store (commit packing
  *     the fp8 payload and scales into one row);

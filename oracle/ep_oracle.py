@@ -21,13 +21,14 @@ dispatch/combine", unless stated otherwise):
   to zero: the commit on masked ``topk_idx``;
 * the packed fp8 row (payload, then the per-128-element fp32 scales, padded
   to 16 bytes) written in one store: the commit packing payload and scales;
-* per-token, per-128-element scales (DeepEP's per_token_cast_to_fp8 layout):
-  the PR description's opening paragraph;
+* one scale per token and per run of 128 elements (the layout of DeepEP's
+  per_token_cast_to_fp8): the PR description's opening paragraph;
 * rows deduplicated per (token, destination), each carrying the token's
   local experts as a K-wide list: the Design section and the commit adding
   receive stats and combine bias;
-* a token's local-expert rows summed before the cross-destination sum: the
-  commit adding the expanded combine (``kDoExpandedSend``).
+* the rows of one token that share a destination added together first, then
+  the destinations' partial sums: the commit adding the expanded combine
+  (``kDoExpandedSend``).
 
 Readings where the pages are silent (each repeated at its function):
 * rows inside one destination segment are ordered by ascending (token, k);
@@ -391,8 +392,9 @@ def combine_grouped(
     P_g = sum over k ascending with (t,k) valid and in group g of
     w[t,k] * y[slot[t,k]]; every product and sum is one fp32 rounding; each
     P_g starts from +0 and the cross-group total from +0 or the bias.  A token's rows inside one group are summed
-    before the cross-group sum, as the expanded combine sums a token's
-    local-expert rows before sending one row per destination."""
+    before the cross-group sum, the order of the expanded combine, which adds
+    up a token's rows on one destination before that destination's single
+    row goes out."""
     y = np.asarray(y_u16, dtype=np.uint16)
     idx = np.asarray(topk_idx, dtype=np.int64)
     slot = np.asarray(slot, dtype=np.int64)

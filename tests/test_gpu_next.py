@@ -100,7 +100,7 @@ def test_expert_row_list_overflow():
 
 @pytest.mark.parametrize("T", [3000, 150])  # two launches; one fused block
 def test_cumulative_recv_stats(T):
-    """Three accumulating layouts with a quarter of the selections masked."""
+    """Three accumulating layouts; 25% of the selections are masked."""
     w = W.by_name("pages").replace(T=T, mask_p=0.25)
     stats = torch.zeros(w.E, dtype=torch.int32, device=DEV)
     want = np.zeros(w.E, np.int64)

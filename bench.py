@@ -37,23 +37,53 @@ def algorithmic_bytes(T, H, K, E, n_sel, fp8_row_bytes):
     return {"layout": layout, "dispatch_fp8": disp_fp8, "dispatch_bf16": disp_bf16, "combine": combine}
 
 
+def _code_only(text):
+    """C/C++/HIP source with its comments and all whitespace removed (string
+    and character literals kept as written), so that a comment edit does not
+    count as a change of the code."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            if not c.isspace():
+                out.append(c)
+            i += 1
+    return "".join(out)
+
+
+def source_hash(files):
+    """First 16 hex digits of the sha256 of the listed sources' code (comments
+    and whitespace excluded, see _code_only), in the order given."""
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode("utf-8"))
+    return h.hexdigest()[:16]
+
+
 def counted_traffic(op, workload):
     """HBM bytes per launch of `op` from the committed FETCH_SIZE/WRITE_SIZE
     passes (profiles/traffic_<op>_<workload>.json), or None when there is no
-    such record or the kernel sources changed since the counters were taken
-    (the record keeps a hash of the sources it was measured on)."""
-    import hashlib
-
+    such record or the kernel code changed since the counters were taken (the
+    record keeps source_hash() of the sources it was measured on)."""
     path = os.path.join(ROOT, "profiles", f"traffic_{op}_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         rec = json.load(fh)
-    h = hashlib.sha256()
-    for f in rec.get("sources", []):
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
-    if h.hexdigest()[:16] != rec.get("source_sha256_16"):
+    if source_hash(rec.get("sources", [])) != rec.get("source_sha256_16"):
         return None
     return rec.get("bytes_per_launch")
 

@@ -286,11 +286,11 @@ hipError_t combine_v(const CombineArgs& a, hipStream_t s) {
   // waves: 174.9 against 176.7 us with 4-wave blocks of 29 KiB, two biases
   // 185.1 against 188.0 us.  At 4 waves per SIMD (16 blocks of 10 KiB) the
   // bench shape gains another 1.0 us but the skewed, masked routing loses
-  // 4.6 us (162.9 against 158.3), so 5 it stays.  With fewer rows per token fewer rows are open
-  // per wave, and the cap costs: hidden 4096, top-4 of 64, 4096 tokens, cold
-  // caches: 35.7 us capped, 33.0 uncapped.  The grouped order is best
-  // uncapped in 4-wave blocks (4 waves per SIMD: 1528 against 1437 us at
-  // 65,536 tokens; single-wave blocks 1474 us).
+  // 4.6 us (162.9 against 158.3), so 5 it stays.  With fewer rows per token
+  // fewer rows are open per wave, and the cap costs: hidden 4096, top-4 of
+  // 64, 4096 tokens, cold caches: 35.7 us capped, 33.0 uncapped.  The
+  // grouped order is best uncapped in 4-wave blocks (4 waves per SIMD: 1528
+  // against 1437 us at 65,536 tokens; single-wave blocks 1474 us).
   if (!GROUPED && a.K >= 8) {
     constexpr auto kern = k_combine<KMAX, VE, GROUPED, U, NB, kWave>;
     kern<<<wave_per_item_blocks(items, 1), kWave, 8000, s>>>(a, nchunks, items);

@@ -33,3 +33,10 @@ def test_algorithmic_bytes_pages_shape():
     n_sel = T * K
     got = bench.algorithmic_bytes(T, H, K, E, n_sel, 7392)
     assert got["combine"] == n_sel * H * 2 + T * K * 8 + T * H * 2 == 1_057_488_896
+
+
+def test_more_than_one_gpu_is_refused(capsys):
+    """bench.py measures one GPU's share; --gpus N > 1 exits with a message
+    and a nonzero status before touching the GPU."""
+    assert bench.main(["--gpus", "2"]) == 2
+    assert "one GPU" in capsys.readouterr().err
